@@ -1,0 +1,97 @@
+"""Pins for the oracle's fp8 decode tables (CPU only).
+
+The tables are pinned to: a second, independent construction (the ULP ladder);
+hand-derived anchor codes stored under tests/golden/ with their citation; the
+library cast of torch, a special case that must agree on every code; and a
+negative control showing that the pins reject the wrong-bias decoder the pages
+warn about ("fp8 KV cache in the in-tree prefill kernel", Architecture / design
+notes, the vec_cast paragraph).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_anchors.txt")
+
+
+def _anchors():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fmt, code, val = line.split()
+            rows.append((fmt, int(code, 16), float(val)))
+    return rows
+
+
+def _same(a, b):
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1, a) == math.copysign(1, b)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_two_constructions_agree(fmt):
+    a = fp8.table_closed_form(fmt)
+    b = fp8.table_ulp_ladder(fmt)
+    for c in range(256):
+        assert _same(a[c], b[c]), (fmt, hex(c), a[c], b[c])
+
+
+def test_anchor_codes():
+    rows = _anchors()
+    assert len(rows) >= 20
+    for fmt, code, val in rows:
+        got = fp8.fp8_table(fmt)[code]
+        assert _same(got, val), (fmt, hex(code), got, val)
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_library_cast_agrees(fmt, tdt):
+    ref = torch.arange(256, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
+    t = fp8.fp8_table(fmt)
+    for c in range(256):
+        assert _same(t[c], ref[c]), (fmt, hex(c), t[c], ref[c])
+
+
+def test_wrong_bias_is_caught():
+    """Negative control: the fnuz bias (8) applied to OCP e4m3 data gives
+    0x38 = 0.5, which the anchors must reject."""
+    wrong = fp8.table_closed_form("e4m3", bias=8)
+    assert wrong[0x38] == 0.5
+    bad = [c for f, c, v in _anchors() if f == "e4m3" and not _same(wrong[c], v)]
+    assert bad, "the anchors did not notice a wrong exponent bias"
+
+
+def test_denormals_present_and_ordered():
+    for fmt, nsub in (("e4m3", 7), ("e5m2", 3)):
+        t = fp8.fp8_table(fmt)
+        sub = t[1:1 + nsub]
+        assert np.all(sub > 0) and np.all(np.diff(sub) > 0)
+        # equally spaced by the smallest subnormal
+        assert np.allclose(np.diff(np.concatenate([[0.0], sub])), sub[0], rtol=0, atol=0)
+        pos = t[:0x7F] if fmt == "e4m3" else t[:0x7C]
+        assert np.all(np.diff(pos) > 0)  # magnitudes increase with the code
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_every_finite_code_is_exact_in_2byte_types(fmt):
+    """Every finite fp8 value is exactly an fp16 and a bf16 value, so a kernel
+    may widen the raw code into q's 2-byte type with no rounding."""
+    t = fp8.fp8_table(fmt)
+    fin = t[np.isfinite(t)]
+    assert np.array_equal(fin.astype(np.float16).astype(np.float64), fin)
+    bf = torch.from_numpy(fin).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf, fin)
+
+
+def test_max_finite():
+    assert fp8.max_finite("e4m3") == 448.0
+    assert fp8.max_finite("e5m2") == 57344.0
