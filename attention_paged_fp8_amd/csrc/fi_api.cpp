@@ -1,0 +1,399 @@
+// Host front end of the C ABI declared in include/fi.h: argument checks in a
+// fixed order (no HIP call before they pass), the split-KV plan, and the
+// kernel launches.
+//
+// The refusal rules and their wording follow "fp8 KV cache in the in-tree
+// prefill kernel" (AMD-Ecosystem/flashinfer PR #368), sections Refusals and
+// Architecture / design notes: q and o are 2-byte floats; the output is never
+// fp8 ("Enable Hopper FA3 FP8 attention in decode.py", flashinfer PR #2148,
+// Walkthrough); k and v must share a dtype; int8/uint8 KV has no float
+// interpretation; a 2-byte KV must equal q for prefill while decode converts
+// it; nothing is ever cast silently.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "fi.h"
+#include "fi_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fi_status fail(fi_status st, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = std::string(fn) + ": " + buf;
+  return st;
+}
+
+const char* dtype_name(fi_dtype d) {
+  switch (d) {
+    case FI_DTYPE_DEFAULT: return "default";
+    case FI_F16: return "float16";
+    case FI_BF16: return "bfloat16";
+    case FI_F8_E4M3: return "float8_e4m3fn";
+    case FI_F8_E5M2: return "float8_e5m2";
+    case FI_F32: return "float32";
+    case FI_I8: return "int8";
+    case FI_U8: return "uint8";
+    case FI_F8_E4M3_FNUZ: return "float8_e4m3fnuz";
+    case FI_F8_E5M2_FNUZ: return "float8_e5m2fnuz";
+  }
+  return "unknown";
+}
+
+bool is_2byte(fi_dtype d) { return d == FI_F16 || d == FI_BF16; }
+bool is_ocp_fp8(fi_dtype d) { return d == FI_F8_E4M3 || d == FI_F8_E5M2; }
+bool is_any_fp8(fi_dtype d) {
+  return is_ocp_fp8(d) || d == FI_F8_E4M3_FNUZ || d == FI_F8_E5M2_FNUZ;
+}
+int elem_bytes(fi_dtype d) { return is_2byte(d) ? 2 : 1; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks 1-5 of the documented order.  `prefill` enables the 2-byte rule.
+fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_dtype v, bool prefill) {
+  if (!is_2byte(q)) {
+    if (is_any_fp8(q))
+      return fail(FI_E_DTYPE, fn, "q has dtype %s; an fp8 query is not supported (q must be float16 or bfloat16, "
+                  "and it is never cast silently)", dtype_name(q));
+    return fail(FI_E_DTYPE, fn, "q has dtype %s; q must be float16 or bfloat16", dtype_name(q));
+  }
+  if (*o == FI_DTYPE_DEFAULT) *o = q;
+  if (is_any_fp8(*o))
+    return fail(FI_E_DTYPE, fn, "o has dtype %s; an fp8 output is not supported (o must be float16 or bfloat16)",
+                dtype_name(*o));
+  if (!is_2byte(*o)) return fail(FI_E_DTYPE, fn, "o has dtype %s; o must be float16 or bfloat16", dtype_name(*o));
+  if (k != v) return fail(FI_E_DTYPE, fn, "k has dtype %s but v has dtype %s", dtype_name(k), dtype_name(v));
+  if (k == FI_I8 || k == FI_U8)
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be float16, "
+                "bfloat16, float8_e4m3fn or float8_e5m2", dtype_name(k));
+  if (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ)
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; this library decodes OCP "
+                "float8_e4m3fn / float8_e5m2", dtype_name(k));
+  if (!is_2byte(k) && !is_ocp_fp8(k))
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s; KV must be float16, bfloat16, float8_e4m3fn or float8_e5m2",
+                dtype_name(k));
+  if (prefill && is_2byte(k) && k != q)
+    return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; prefill needs a 2-byte KV cache of the "
+                "query's dtype (fp8 KV is widened on load)", dtype_name(q), dtype_name(k));
+  return FI_OK;
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+fi_status check_heads(const char* fn, int32_t hqo, int32_t hkv, int32_t d) {
+  if (hqo <= 0 || hkv <= 0) return fail(FI_E_SHAPE, fn, "head counts must be positive (num_qo_heads=%d, num_kv_heads=%d)", hqo, hkv);
+  if (hqo % hkv != 0)
+    return fail(FI_E_SHAPE, fn, "num_qo_heads=%d is not a multiple of num_kv_heads=%d", hqo, hkv);
+  if (d != 64 && d != 128) return fail(FI_E_SHAPE, fn, "head_dim=%d; supported head_dim values are 64 and 128", d);
+  return FI_OK;
+}
+
+fi_status check_scales(const char* fn, float k_scale, float v_scale, float sm_scale) {
+  if (!std::isfinite(k_scale) || !(k_scale > 0.f)) return fail(FI_E_ARG, fn, "k_scale=%g must be finite and > 0", k_scale);
+  if (!std::isfinite(v_scale) || !(v_scale > 0.f)) return fail(FI_E_ARG, fn, "v_scale=%g must be finite and > 0", v_scale);
+  if (!std::isfinite(sm_scale)) return fail(FI_E_ARG, fn, "sm_scale=%g must be finite (<= 0 selects 1/sqrt(head_dim))", sm_scale);
+  return FI_OK;
+}
+
+// Checks on the paged cache: shape, pointers, alignment and the host page table.
+// On success *max_kv and *total_kv hold the longest and the summed kv_len.
+fi_status check_paged(const char* fn, int32_t batch, const fi_paged_kv* kv, int64_t* max_kv, int64_t* total_kv) {
+  const int eb = elem_bytes(kv->k_dtype);
+  if (!pow2(kv->page_size) || kv->page_size > 128)
+    return fail(FI_E_SHAPE, fn, "page_size=%d; page_size must be a power of two from 1 to 128", kv->page_size);
+  if (kv->num_pages < 0) return fail(FI_E_SHAPE, fn, "num_pages=%d is negative", kv->num_pages);
+  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0)
+    return fail(FI_E_SHAPE, fn, "strides must be positive (page %lld, token %lld, head %lld)",
+                (long long)kv->stride_page, (long long)kv->stride_token, (long long)kv->stride_head);
+  if ((kv->stride_page * eb) % 16 || (kv->stride_token * eb) % 16 || (kv->stride_head * eb) % 16)
+    return fail(FI_E_ARG, fn, "K/V strides must give 16-byte aligned rows (page %lld, token %lld, head %lld elements "
+                "of %d bytes)", (long long)kv->stride_page, (long long)kv->stride_token, (long long)kv->stride_head, eb);
+  if (batch > 0) {
+    if (!kv->k || !kv->v) return fail(FI_E_ARG, fn, "k and v page pools must not be NULL");
+    if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(FI_E_ARG, fn, "k and v page pools must be 16-byte aligned");
+    if (!kv->indptr || !kv->indices || !kv->last_page_len)
+      return fail(FI_E_ARG, fn, "indptr, indices and last_page_len (device) must not be NULL");
+    if (!kv->indptr_h || !kv->last_page_len_h)
+      return fail(FI_E_ARG, fn, "indptr_h and last_page_len_h (host copies) must not be NULL");
+  }
+  int64_t mx = 0, tot = 0;
+  if (batch > 0 && kv->indptr_h[0] < 0) return fail(FI_E_ARG, fn, "indptr[0]=%d is negative", kv->indptr_h[0]);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t a = kv->indptr_h[i], e = kv->indptr_h[i + 1];
+    if (e < a) return fail(FI_E_ARG, fn, "indptr is decreasing at request %d (%d > %d)", i, a, e);
+    const int32_t np = e - a;
+    int64_t len = 0;
+    if (np > 0) {
+      const int32_t lp = kv->last_page_len_h[i];
+      if (lp < 1 || lp > kv->page_size)
+        return fail(FI_E_ARG, fn, "last_page_len[%d]=%d is outside [1, page_size=%d]", i, lp, kv->page_size);
+      len = (int64_t)(np - 1) * kv->page_size + lp;
+    }
+    if (len >= (1ll << 30)) return fail(FI_E_SHAPE, fn, "request %d has %lld tokens; at most 2^30 - 1 are supported", i, (long long)len);
+    mx = len > mx ? len : mx;
+    tot += len;
+  }
+  *max_kv = mx;
+  *total_kv = tot;
+  return FI_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+constexpr int kMinAutoChunk = 256;   // smallest chunk the workspace bound allows for
+constexpr int kTargetWorkgroups = 2048;
+
+// Split-KV plan: tokens per chunk.  0 split => chunk covers the longest request.
+int64_t plan_chunk(int64_t max_kv, int64_t total_kv, int64_t units_per_token, bool have_ws) {
+  const int64_t q = fi::kChunkQuantum;
+  const int64_t whole = std::max<int64_t>(q, round_up(std::max<int64_t>(max_kv, 1), q));
+  if (!have_ws) return whole;
+  const char* env = std::getenv("FI_SPLIT_KV");
+  if (env && *env && std::strcmp(env, "auto") != 0) {
+    if (std::strcmp(env, "off") == 0) return whole;
+    const long n = std::strtol(env, nullptr, 10);
+    if (n > 0) return std::min(whole, std::max<int64_t>(q, round_up(n, q)));
+  }
+  const int64_t work = total_kv * units_per_token;
+  int64_t c = round_up(std::max<int64_t>(1, ceil_div(work, kTargetWorkgroups)), q);
+  c = std::max<int64_t>(c, kMinAutoChunk);
+  return std::min(c, whole);
+}
+
+size_t partial_bytes(int64_t batch, int64_t max_chunks, int64_t hqo, int64_t d) {
+  if (max_chunks <= 1) return 0;
+  return (size_t)(batch * max_chunks * hqo * (d + 1) * 4);
+}
+
+fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_dtype kv_dtype, fi_dtype o_dtype,
+                     int32_t batch, int32_t head_dim, int64_t max_kv, int64_t total_kv, void* workspace,
+                     size_t workspace_bytes, float sm_scale, float k_scale, float v_scale, hipStream_t stream) {
+  const int nsub = (p.group + fi::kDecodeRows - 1) / fi::kDecodeRows;
+  p.nsub = nsub;
+  const int64_t chunk = plan_chunk(max_kv, total_kv, (int64_t)p.num_kv_heads * nsub, workspace != nullptr);
+  const int64_t max_chunks = std::max<int64_t>(1, ceil_div(max_kv, chunk));
+  const size_t need = partial_bytes(batch, max_chunks, p.num_qo_heads, head_dim);
+  if (need > 0 && workspace_bytes < need)
+    return fail(FI_E_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the %zu bytes this split needs "
+                "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
+  if (max_chunks > 0x7fffffff) return fail(FI_E_SHAPE, fn, "too many chunks");
+  const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
+  if (max_chunks * p.num_kv_heads * nsub * (int64_t)batch > 0x7fffffff)
+    return fail(FI_E_SHAPE, fn, "the split needs more than 2^31 workgroups");
+  p.chunk = (int32_t)chunk;
+  p.max_chunks = (int32_t)max_chunks;
+  p.batch = batch;
+  p.scale_log2 = scale * k_scale * fi::kLog2eHost;
+  p.v_scale = v_scale;
+  p.part_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  p.part_lse = need ? reinterpret_cast<float*>(workspace) + (size_t)batch * max_chunks * p.num_qo_heads * head_dim
+                    : nullptr;
+  if (batch == 0) return FI_OK;
+  hipError_t err = fi::launch_decode(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, stream);
+  if (err != hipSuccess) return fail(FI_E_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(err));
+  if (max_chunks > 1) {
+    fi::MergeParams mp{};
+    mp.o = p.o;
+    mp.lse = p.lse;
+    mp.part_o = p.part_o;
+    mp.part_lse = p.part_lse;
+    mp.indptr = p.indptr;
+    mp.last_page_len = p.last_page_len;
+    mp.page_size = p.page_size;
+    mp.single_kv_len = p.single_kv_len;
+    mp.num_qo_heads = p.num_qo_heads;
+    mp.chunk = p.chunk;
+    mp.max_chunks = p.max_chunks;
+    mp.v_scale = v_scale;
+    err = fi::launch_merge(mp, o_dtype, head_dim, batch, stream);
+    if (err != hipSuccess) return fail(FI_E_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(err));
+  }
+  return FI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fi_last_error(void) { return g_err.c_str(); }
+
+size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_kv_len) {
+  if (batch <= 0 || num_qo_heads <= 0 || head_dim <= 0 || max_kv_len <= 0) return 0;
+  // any plan, including a forced FI_SPLIT_KV chunk, uses chunks of at least kChunkQuantum tokens
+  const int64_t max_chunks = ceil_div(max_kv_len, fi::kChunkQuantum);
+  return partial_bytes(batch, std::max<int64_t>(max_chunks, 2), num_qo_heads, head_dim);
+}
+
+fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
+                                const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "fi_batch_decode_paged";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, false);
+  if (st != FI_OK) return st;
+  if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is outside [0, 2^31)", batch);
+  if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
+  if (batch > 0) {
+    if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
+    if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
+  }
+  if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
+  int64_t max_kv = 0, total_kv = 0;
+  if ((st = check_paged(fn, batch, kv, &max_kv, &total_kv)) != FI_OK) return st;
+  const int eb = elem_bytes(kv->k_dtype);
+  fi::DecodeParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(kv->k);
+  p.v = reinterpret_cast<const uint8_t*>(kv->v);
+  p.sp = kv->stride_page * eb;
+  p.st = kv->stride_token * eb;
+  p.sh = kv->stride_head * eb;
+  p.indptr = kv->indptr;
+  p.indices = kv->indices;
+  p.last_page_len = kv->last_page_len;
+  p.page_shift = ilog2(kv->page_size);
+  p.page_size = kv->page_size;
+  p.single_kv_len = 0;
+  p.num_qo_heads = num_qo_heads;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.group = num_qo_heads / kv->num_kv_heads;
+  return run_decode(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, kv->head_dim, max_kv, total_kv, workspace,
+                    workspace_bytes, sm_scale, kv->k_scale, kv->v_scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const void* v, fi_dtype k_dtype,
+                           fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float k_scale, float v_scale, void* o, fi_dtype o_dtype, float* lse,
+                           float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "fi_single_decode";
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, k_dtype, v_dtype, false);
+  if (st != FI_OK) return st;
+  if ((st = check_heads(fn, num_qo_heads, num_kv_heads, head_dim)) != FI_OK) return st;
+  if (kv_len < 0 || kv_len >= (1 << 30)) return fail(FI_E_SHAPE, fn, "kv_len=%d is outside [0, 2^30)", kv_len);
+  if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
+  if (kv_len > 0 && (!k || !v)) return fail(FI_E_ARG, fn, "k and v must not be NULL");
+  if (kv_len > 0 && (!aligned16(k) || !aligned16(v))) return fail(FI_E_ARG, fn, "k and v must be 16-byte aligned");
+  if ((st = check_scales(fn, k_scale, v_scale, sm_scale)) != FI_OK) return st;
+  const int eb = elem_bytes(k_dtype);
+  fi::DecodeParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(k);
+  p.v = reinterpret_cast<const uint8_t*>(v);
+  p.sp = 0;
+  p.st = (int64_t)num_kv_heads * head_dim * eb;
+  p.sh = (int64_t)head_dim * eb;
+  p.indptr = nullptr;
+  p.indices = nullptr;
+  p.last_page_len = nullptr;
+  p.page_shift = 30;
+  p.page_size = 1 << 30;
+  p.single_kv_len = kv_len;
+  p.num_qo_heads = num_qo_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_qo_heads / num_kv_heads;
+  return run_decode(fn, p, q_dtype, k_dtype, o_dtype, 1, head_dim, kv_len, kv_len, workspace, workspace_bytes,
+                    sm_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
+                                 const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                 const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                 float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "fi_batch_prefill_paged";
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, true);
+  if (st != FI_OK) return st;
+  if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is negative", batch);
+  if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
+  if (batch > 0) {
+    if (!qo_indptr || !qo_indptr_h) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  }
+  if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
+  int64_t max_kv = 0, total_kv = 0;
+  if ((st = check_paged(fn, batch, kv, &max_kv, &total_kv)) != FI_OK) return st;
+  int64_t max_qo = 0, total_qo = 0;
+  if (batch > 0 && qo_indptr_h[0] < 0) return fail(FI_E_ARG, fn, "qo_indptr[0]=%d is negative", qo_indptr_h[0]);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t n = (int64_t)qo_indptr_h[i + 1] - qo_indptr_h[i];
+    if (n < 0) return fail(FI_E_ARG, fn, "qo_indptr is decreasing at request %d", i);
+    max_qo = n > max_qo ? n : max_qo;
+    total_qo += n;
+  }
+  if (total_qo > 0) {
+    if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
+    if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
+  }
+  if (batch == 0 || max_qo == 0) return FI_OK;
+  const int eb = elem_bytes(kv->k_dtype);
+  fi::PrefillParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(kv->k);
+  p.v = reinterpret_cast<const uint8_t*>(kv->v);
+  p.sp = kv->stride_page * eb;
+  p.st = kv->stride_token * eb;
+  p.sh = kv->stride_head * eb;
+  p.qo_indptr = qo_indptr;
+  p.indptr = kv->indptr;
+  p.indices = kv->indices;
+  p.last_page_len = kv->last_page_len;
+  p.page_shift = ilog2(kv->page_size);
+  p.page_size = kv->page_size;
+  p.num_qo_heads = num_qo_heads;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.group = num_qo_heads / kv->num_kv_heads;
+  p.heads_per_wg = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
+  p.q_per_wg = 128 / p.heads_per_wg;
+  p.n_qblocks = (int32_t)ceil_div(max_qo, p.q_per_wg);
+  p.causal = causal ? 1 : 0;
+  const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)kv->head_dim);
+  p.scale_log2 = scale * kv->k_scale * fi::kLog2eHost;
+  p.v_scale = kv->v_scale;
+  if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
+                                       (long long)max_qo, 65535 * p.q_per_wg);
+  hipError_t err = fi::launch_prefill(p, q_dtype, kv->k_dtype, o_dtype, kv->head_dim, batch,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));
+  return FI_OK;
+}
+
+fi_status fi_fp8_widen(const uint8_t* codes, int64_t n, fi_dtype src, fi_dtype dst, void* out, void* stream) {
+  static const char* fn = "fi_fp8_widen";
+  if (!is_ocp_fp8(src)) return fail(FI_E_DTYPE, fn, "src has dtype %s; src must be float8_e4m3fn or float8_e5m2", dtype_name(src));
+  if (!is_2byte(dst)) return fail(FI_E_DTYPE, fn, "dst has dtype %s; dst must be float16 or bfloat16", dtype_name(dst));
+  if (n < 0) return fail(FI_E_SHAPE, fn, "n=%lld is negative", (long long)n);
+  if (n == 0) return FI_OK;
+  if (!codes || !out) return fail(FI_E_ARG, fn, "codes and out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(FI_E_ARG, fn, "out must be 2-byte aligned");
+  hipError_t err = fi::launch_fp8_widen(codes, n, src, dst, out, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FI_E_HIP, fn, "widen kernel launch failed: %s", hipGetErrorString(err));
+  return FI_OK;
+}
+
+}  // extern "C"

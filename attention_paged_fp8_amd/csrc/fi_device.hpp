@@ -1,0 +1,188 @@
+// Device-side helpers for the gfx950 kernels: element widening, MFMA wrappers,
+// exp2/log2 and cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fi_internal.h"
+
+namespace fi {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, x);
+}
+
+// 16-byte global loads; the streaming form marks the lines non-temporal (each
+// KV byte is read once per call).
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return bitcast<uint4>(*reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  return bitcast<uint4>(__builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
+// ---------------------------------------------------------------------------
+// fp8 -> 2-byte widening.
+//
+// gfx950 converts OCP fp8 natively: v_cvt_scalef32_pk_{f16,bf16}_{fp8,bf8}
+// takes two codes (the low or the high 16-bit half of a dword, per word_sel)
+// and multiplies by an fp32 scale.  With scale 1.0 the result is the exact
+// value: every finite e4m3 / e5m2 value, subnormals included, is representable
+// in fp16 and in bf16 (the oracle's tables test this), so no rounding occurs.
+// The k / v scales are not applied here but in fp32 (logit scale and output).
+// ---------------------------------------------------------------------------
+// The two word_sel immediates must be compile-time constants.
+template <bool QBF16, int KVF>
+__device__ __forceinline__ uint2 widen4(uint32_t w) {
+  uint2 r;
+  if constexpr (!QBF16) {
+    if constexpr (KVF == FMT_E4M3) {
+      r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+      r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+    } else {
+      r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false));
+      r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true));
+    }
+  } else {
+    if constexpr (KVF == FMT_E4M3) {
+      r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    } else {
+      r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false));
+      r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true));
+    }
+  }
+  return r;
+}
+
+// 8 fp8 codes (two dwords) -> one MFMA operand of 8 2-byte values.
+template <bool QBF16, int KVF>
+__device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {
+  uint2 a = widen4<QBF16, KVF>(lo);
+  uint2 b = widen4<QBF16, KVF>(hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Exact split of fp16 values into bf16 pairs: v == hi + lo with hi = bf16(v)
+// (round to nearest even) and lo = bf16(v - hi).  An fp16 value has 11
+// significant bits; hi keeps 8 and the residual has at most 3, so lo holds it
+// exactly, and bf16's exponent range covers every fp16 value.  Used when an
+// fp16 operand meets a bf16 one (mixed 2-byte decode): the MFMA runs in bf16 on
+// hi and lo, so no value is rounded and none can overflow.
+__device__ __forceinline__ void split_f16x2(uint32_t w, uint32_t& hi, uint32_t& lo) {
+  const f16x2_t h = bitcast<f16x2_t>(w);
+  const float a = (float)h.x, b = (float)h.y;
+  const __bf16 ah = (__bf16)a, bh = (__bf16)b;
+  const bf16x2_t vh = {ah, bh};
+  const bf16x2_t vl = {(__bf16)(a - (float)ah), (__bf16)(b - (float)bh)};
+  hi = bitcast<uint32_t>(vh);
+  lo = bitcast<uint32_t>(vl);
+}
+
+__device__ __forceinline__ void split_f16x8(uint4 x, uint4& hi, uint4& lo) {
+  split_f16x2(x.x, hi.x, lo.x);
+  split_f16x2(x.y, hi.y, lo.y);
+  split_f16x2(x.z, hi.z, lo.z);
+  split_f16x2(x.w, hi.w, lo.w);
+}
+
+// ---------------------------------------------------------------------------
+// LDS transposed reads (gfx950).  Within each group of 16 lanes:
+//  * lds_tr8  (ds_read_b64_tr_b8):  lanes 2r and 2r+1 give the addresses of the
+//    two 8-byte halves of row r (r = 0..7); lane i receives byte column i of
+//    the 8 rows, row r in byte r.
+//  * lds_tr16 (ds_read_b64_tr_b16): lanes 4r..4r+3 give the four 8-byte pieces
+//    of row r (r = 0..3); lane i receives 16-bit column i of the 4 rows.
+// Rows are whatever the addresses name, so any token order can be gathered.
+// ---------------------------------------------------------------------------
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
+  const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
+  return bitcast<uint2>(r);
+}
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t* p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return bitcast<uint2>(r);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (operands as raw dwords).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scalars
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round an fp32 to q's 2-byte type and return (bits, value as fp32).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF16) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return bitcast<uint32_t>(r);
+  } else {
+    f16x2_t r = {(_Float16)a, (_Float16)b};
+    return bitcast<uint32_t>(r);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float2 unpack2(uint32_t w) {
+  if constexpr (BF16) {
+    return make_float2(bitcast<float>(w << 16), bitcast<float>(w & 0xffff0000u));
+  } else {
+    f16x2_t h = bitcast<f16x2_t>(w);
+    return make_float2((float)h.x, (float)h.y);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_bits(float a) {
+  if constexpr (BF16) {
+    return bitcast<uint16_t>((__bf16)a);
+  } else {
+    return bitcast<uint16_t>((_Float16)a);
+  }
+}
+
+// Cross-lane max / sum over lanes l, l^16, l^32, l^48 (ds_swizzle-free: bpermute).
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+}  // namespace fi

@@ -1,0 +1,258 @@
+"""Benchmark of the paged fp8-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+A step is one fi_batch_decode_paged call (page-table gather, fp8 widening,
+QK^T and PV on MFMA, online softmax, split-KV partials and their merge) on the
+batch-decode workload: 64 requests, kv_len uniform in [512, 4096], 32 q / 8 kv
+heads, head_dim 128, page 16 with shuffled pages, bf16 q/o, fp8 e4m3 K/V.
+Inputs are resident in HBM before timing; the K/V pools are rotated over
+several identical copies so that no step finds the previous step's pages in the
+256 MB last-level cache.  `value` is HBM GB/s counting the algorithmic bytes:
+every valid K and V element once at 1 byte (fp8), q, o, lse and the page table
+("fp8 KV cache in the in-tree prefill kernel", AMD-Ecosystem/flashinfer PR
+#368, Tests, docs, benchmark: the fp8 byte count).
+
+The same JSON line carries the causal-prefill figure (16 requests, qo_len
+256..1024 plus a prefix of 0..2048, 32/8 heads, head_dim 128, e4m3 K/V, f16):
+MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head,
+and the float64 oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS_16 = 2500.0   # MI355X dense fp16 / bf16 MFMA
+METRIC = "decode fp8-KV HBM GB/s (% of peak); prefill TFLOP/s (% of MFMA peak)"
+ELEM = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1}
+
+
+def decode_bytes(w: dict) -> int:
+    """Algorithmic bytes of one decode call."""
+    eb = ELEM[w["kv_dtype"]]
+    kv = int(w["kv_lens"].sum()) * w["num_kv_heads"] * w["head_dim"] * eb * 2
+    ntok = int(w["qo_indptr"][-1])
+    qo = ntok * w["num_qo_heads"] * w["head_dim"] * (ELEM[w["q_dtype"]] + ELEM[w["o_dtype"]])
+    lse = ntok * w["num_qo_heads"] * 4
+    table = 4 * (len(w["indices"]) + 2 * len(w["kv_lens"]) + 1)
+    return kv + qo + lse + table
+
+
+def visible_pairs(w: dict, causal: bool = True) -> int:
+    tot = 0
+    for qo, kv in zip(w["qo_lens"], w["kv_lens"]):
+        qo, kv = int(qo), int(kv)
+        if not causal:
+            tot += qo * kv
+            continue
+        r = np.arange(qo)
+        tot += int(np.clip(r + 1 + (kv - qo), 0, kv).sum())
+    return tot
+
+
+def prefill_flops(w: dict, causal: bool = True) -> int:
+    return 4 * w["head_dim"] * w["num_qo_heads"] * visible_pairs(w, causal)
+
+
+def _upload(w, dev, copies: int):
+    import torch
+
+    from attention_paged_fp8_amd import fi
+
+    t2 = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+    def pool(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        if w["kv_dtype"] in t2:
+            t = t.view(torch.int16).view(t2[w["kv_dtype"]])
+        return t.to(dev)
+
+    q = torch.from_numpy(w["q"].view(np.int16)).view(t2[w["q_dtype"]]).to(dev)
+    idx = {n: torch.from_numpy(np.ascontiguousarray(w[n], dtype=np.int32)).to(dev)
+           for n in ("indptr", "indices", "last_page_len", "qo_indptr")}
+    kvs, keep = [], []
+    for _ in range(copies):
+        k, v = pool(w["k_pool"]), pool(w["v_pool"])
+        s, kk = fi.make_paged_kv(k, v, idx["indptr"], idx["indices"], idx["last_page_len"], k_scale=w["k_scale"],
+                                 v_scale=w["v_scale"], kv_dtype=w["kv_dtype"], indptr_h=w["indptr"],
+                                 last_page_len_h=w["last_page_len"])
+        kvs.append(s)
+        keep.append((k, v, kk))
+    return q, idx, kvs, keep
+
+
+def _time_calls(fn, n_copies, steps, warmup, stream):
+    """Warm up, then time exactly `steps` calls: wall clock bracketed by
+    synchronize, and HIP events around every call on the launch stream."""
+    import torch
+
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(i % n_copies)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return wall_ms, ev
+
+
+def run_decode_bench(steps, warmup, copies):
+    import torch
+
+    from attention_paged_fp8_amd import fi
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(2)
+    q, idx, kvs, keep = _upload(w, dev, copies)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    nws = fi.fi_decode_workspace_bytes(len(w["kv_lens"]), w["num_qo_heads"], w["head_dim"], int(w["kv_lens"].max()))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        fi.fi_batch_decode_paged(q, kvs[i], o, lse=lse, workspace=ws, stream=stream)
+
+    wall_ms, ev = _time_calls(step, copies, steps, warmup, stream)
+    return w, wall_ms, ev
+
+
+def run_prefill_bench(steps, warmup):
+    import torch
+
+    from attention_paged_fp8_amd import fi
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(3)
+    q, idx, kvs, keep = _upload(w, dev, 1)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        fi.fi_batch_prefill_paged(q, idx["qo_indptr"], kvs[0], o, causal=True, lse=lse,
+                                  qo_indptr_h=w["qo_indptr"], stream=stream)
+
+    wall_ms, ev = _time_calls(step, 1, steps, warmup, stream)
+    return w, wall_ms, ev
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The float64 oracle on a bounded sample of the decode workload (whole
+    requests, in order, until about budget_s of CPU time), one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle.attention as OA
+
+    done, t_used, nbytes = 0, 0.0, 0
+    B = len(w["kv_lens"])
+    per_tok = w["num_kv_heads"] * w["head_dim"] * ELEM[w["kv_dtype"]] * 2
+    with threadpool_limits(limits=1):
+        while done < B and t_used < budget_s:
+            t0 = time.perf_counter()
+            OA.batch_decode(w, requests=[done])
+            t_used += time.perf_counter() - t0
+            nbytes += int(w["kv_lens"][done]) * per_tok
+            done += 1
+    gbs = nbytes / t_used / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{done} of {B} requests of the batch-decode workload ({nbytes / 1e6:.1f} MB of fp8 K/V), "
+                       f"{t_used:.1f} s, float64 numpy, 1 thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4, help="identical K/V pool copies rotated across steps")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this library and benchmark run on one GPU only; "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
+        sys.exit(2)
+
+    from attention_paged_fp8_amd import fi
+
+    if not os.path.exists(fi.LIB_PATH):
+        from attention_paged_fp8_amd.build import build
+        build()
+
+    w, wall_ms, ev = run_decode_bench(args.steps, args.warmup, args.copies)
+    nbytes = decode_bytes(w)
+    value = nbytes / (wall_ms * 1e-3) / 1e9
+    ev_ms = float(ev.mean())
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    print(f"# decode: {nbytes / 1e6:.1f} MB per call, wall {wall_ms * 1e3:.1f} us/step, events mean "
+          f"{ev_ms * 1e3:.1f} us (min {ev.min() * 1e3:.1f}, max {ev.max() * 1e3:.1f})", file=sys.stderr, flush=True)
+
+    pw, p_wall, p_ev = run_prefill_bench(args.prefill_steps, 3)
+    flops = prefill_flops(pw)
+    p_ms = float(p_ev.mean())
+    tflops = flops / (p_ms * 1e-3) / 1e12
+    print(f"# prefill: {flops / 1e9:.1f} GFLOP per call, events mean {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w["name"], "batch": 64, "kv_len": "uniform[512,4096]", "total_kv_tokens": int(w["kv_lens"].sum()),
+            "num_qo_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16, "pages": "shuffled",
+            "q_o": "bf16", "kv": "fp8 e4m3 (OCP)", "seed": 2, "kv_pool_copies_rotated": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode_kernel + merge_kernel (one C-ABI call, timed with HIP events on its stream)",
+            "bytes_per_launch": nbytes,
+        },
+        "prefill": {
+            "workload": pw["name"], "tflops": round(tflops, 2), "ms": round(p_ms, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS_16,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS_16, 4), "traffic": None,
+                         "flops_per_launch": flops},
+            "dtype": "f16",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

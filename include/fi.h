@@ -1,0 +1,186 @@
+/*
+ * fi.h -- C ABI of a gfx950 (MI355X) library for batched attention over a
+ * paged KV cache, decode and causal prefill, with fp16/bf16 queries and
+ * outputs and K/V stored as OCP fp8 (e4m3 or e5m2) with per-tensor scales,
+ * widened to the query's 2-byte type as they are loaded.
+ *
+ * The problem statement these calls follow comes from three pages:
+ *   [A] "Enable Hopper FA3 FP8 attention in decode.py" (flashinfer PR #2148):
+ *       the plan()/run() arguments (paged_kv_indptr / indices /
+ *       last_page_len, head counts, head_dim, page_size, q/kv/o dtypes,
+ *       k_scale / v_scale), the output dtype that defaults to the query's and
+ *       is never fp8 (Walkthrough; review comments), the output shape of q
+ *       with V's head_dim (Nitpick comments), the split-KV plan knobs
+ *       fixed_split_size / disable_split_kv (review comments).
+ *   [B] "fallback to fa2 (instead of fa3) for unsupported configuration (bf16
+ *       Q, Fp8 KV)" (flashinfer PR #2536): a 2-byte query against an fp8
+ *       cache is a configuration a library must serve or refuse explicitly.
+ *   [C] "fp8 KV cache in the in-tree prefill kernel" (AMD-Ecosystem/flashinfer
+ *       PR #368): the refusal rules and their sentences (Refusals; Test plan),
+ *       the k_scale / v_scale folds (Test plan), mixed 2-byte decode
+ *       (Architecture / design notes), the OCP exponent biases (Architecture /
+ *       design notes), the paged decode and causal prefill workloads
+ *       (Benchmark results).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers marked [dev] are device (HBM) pointers on the current HIP
+ *    device; [host] pointers are read by the host during the call only.
+ *  - q and o are row-major [tokens, num_qo_heads, head_dim], contiguous.
+ *    Decode has tokens = batch (one query per request); prefill is ragged by
+ *    qo_indptr.  lse is [tokens, num_qo_heads] float32, natural log of the
+ *    sum of exp(scaled logits); it may be NULL.
+ *  - K and V page pools have element strides (stride_page, stride_token,
+ *    stride_head); head_dim is contiguous.  The default layout is
+ *    [num_pages, page_size, num_kv_heads, head_dim] ("NHD").
+ *  - GQA: num_qo_heads % num_kv_heads == 0 and q head h reads kv head
+ *    h / (num_qo_heads / num_kv_heads).
+ *  - Token t of request i lives on page indices[indptr[i] + t / page_size],
+ *    slot t % page_size; the request holds
+ *    (indptr[i+1] - indptr[i] - 1) * page_size + last_page_len[i] tokens,
+ *    or none when it has no pages (then o = 0 and lse = -inf).
+ *  - Real K = stored K * k_scale, real V = stored V * v_scale ([A] review
+ *    comments; [C] Test plan).  The stored fp8 code is widened exactly into
+ *    q's 2-byte type; k_scale is folded into the logit scale and v_scale into
+ *    the output before its single rounding -- the same arithmetic as scaling
+ *    every element, with one rounding fewer.
+ *  - sm_scale <= 0 selects 1/sqrt(head_dim).
+ *  - Causal prefill: query row r of a request with qo_len queries and kv_len
+ *    keys sees key t iff t <= r + kv_len - qo_len (aligned to the end of the
+ *    KV sequence).
+ *  - head_dim is 64 or 128; page_size is a power of two, 1..128; base
+ *    pointers and strides give 16-byte aligned rows.
+ *  - Calls are asynchronous on `stream` (a hipStream_t, NULL = the null
+ *    stream).  The caller owns every buffer and keeps it alive until the
+ *    stream has run the call.  The library allocates no memory and keeps no
+ *    state between calls.  Host arrays must hold the same values as their
+ *    device twins.
+ *
+ * Errors
+ * ------
+ * Every call returns an fi_status.  On any status other than FI_OK no kernel
+ * has been launched and o / lse are untouched (except FI_E_HIP, reported after
+ * a launch failed).  fi_last_error() then returns a sentence naming the call,
+ * the argument(s) and the dtype(s), e.g.
+ *   "fi_batch_decode_paged: k has dtype float16 but v has dtype bfloat16".
+ * Checks run in a fixed order: query dtype, output dtype, k/v dtype match,
+ * KV dtype, (prefill) 2-byte KV equal to q, then shapes, pointers, alignment,
+ * page table and scales, then workspace.
+ */
+#ifndef FI_H_
+#define FI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fi_dtype {
+  FI_DTYPE_DEFAULT = 0, /* output only: the query's dtype ([A] Walkthrough) */
+  FI_F16 = 1,
+  FI_BF16 = 2,
+  FI_F8_E4M3 = 3,      /* OCP e4m3 ("e4m3fn"), bias 7 ([C] design notes) */
+  FI_F8_E5M2 = 4,      /* OCP e5m2, bias 15 */
+  FI_F32 = 5,          /* refused everywhere */
+  FI_I8 = 6,           /* refused: no float interpretation ([C] design notes) */
+  FI_U8 = 7,           /* refused, as int8 */
+  FI_F8_E4M3_FNUZ = 8, /* refused: the gfx942 variant, bias 8 */
+  FI_F8_E5M2_FNUZ = 9  /* refused: the gfx942 variant, bias 16 */
+} fi_dtype;
+
+typedef enum fi_status {
+  FI_OK = 0,
+  FI_E_DTYPE = 1,     /* a dtype or dtype combination is refused */
+  FI_E_SHAPE = 2,     /* a size, head count, head_dim or page_size is invalid */
+  FI_E_ARG = 3,       /* a pointer, alignment, scale or page-table value is invalid */
+  FI_E_WORKSPACE = 4, /* workspace present but smaller than fi_decode_workspace_bytes() */
+  FI_E_HIP = 5        /* the HIP runtime reported an error (message included) */
+} fi_status;
+
+/* The paged K/V cache of one call ([A] plan() arguments). */
+typedef struct fi_paged_kv {
+  const void* k;                /* [dev] K page pool */
+  const void* v;                /* [dev] V page pool (same strides as k) */
+  fi_dtype k_dtype, v_dtype;    /* must be equal */
+  int64_t stride_page;          /* elements between consecutive pages */
+  int64_t stride_token;         /* elements between consecutive slots of a page */
+  int64_t stride_head;          /* elements between consecutive kv heads */
+  int32_t num_pages;            /* pages in each pool */
+  int32_t page_size;            /* power of two, 1..128 */
+  int32_t num_kv_heads;
+  int32_t head_dim;             /* 64 or 128 */
+  const int32_t* indptr;        /* [dev] [batch+1] page ranges per request */
+  const int32_t* indices;       /* [dev] [indptr[batch]] page ids, each < num_pages */
+  const int32_t* last_page_len; /* [dev] [batch] valid slots of the last page, 1..page_size */
+  const int32_t* indptr_h;      /* [host] copy of indptr (planning and checks) */
+  const int32_t* last_page_len_h; /* [host] copy of last_page_len */
+  float k_scale, v_scale;       /* per-tensor, finite and > 0; 1.0 = none */
+} fi_paged_kv;
+
+/* The sentence describing the last non-FI_OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next call on this thread. */
+const char* fi_last_error(void);
+
+/* Bytes of device workspace that fi_batch_decode_paged and fi_single_decode
+ * may use for split-KV partial states, for any call whose longest request has
+ * at most max_kv_len tokens.  Split-KV divides a long request into chunks
+ * processed in parallel and merges their (output, log-sum-exp) states
+ * ([A] review comments: fixed_split_size / disable_split_kv). */
+size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_kv_len);
+
+/* Batched decode: one query token per request against its paged K/V.
+ *   q        [dev] [batch, num_qo_heads, head_dim], q_dtype in {FI_F16, FI_BF16}
+ *   kv       the paged cache; KV dtype in {F16, BF16, E4M3, E5M2}.  A 2-byte KV
+ *            dtype may differ from q's ([C] design notes: mixed 2-byte decode
+ *            is correct); its values are converted to q's type on load.
+ *   o        [dev] [batch, num_qo_heads, head_dim] of o_dtype
+ *            (FI_DTYPE_DEFAULT = q_dtype; fp8 refused)
+ *   lse      [dev] [batch, num_qo_heads] float32, or NULL
+ *   workspace [dev] split-KV scratch, or NULL to process each request in one
+ *            piece (disable_split_kv).  If non-NULL, workspace_bytes must be at
+ *            least fi_decode_workspace_bytes(batch, num_qo_heads, head_dim,
+ *            longest kv_len).
+ * Environment: FI_SPLIT_KV = "off" disables splitting, a positive integer
+ * forces that many tokens per chunk (rounded up to a multiple of 128), unset
+ * or "auto" lets the planner choose (fixed_split_size). */
+fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
+                                const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Batched prefill over the paged cache ([C] Summary and Refusals).
+ *   q          [dev] [qo_indptr[batch], num_qo_heads, head_dim]
+ *   qo_indptr  [dev] [batch+1] query ranges; qo_indptr_h its [host] copy.
+ *   causal     nonzero: mask aligned to the end of the KV sequence.
+ *   A 2-byte KV dtype must equal q_dtype ([C] Refusals: prefill reads KV
+ *   fragments as the query type); fp8 KV is widened on load.
+ *   workspace / workspace_bytes are unused (prefill does not split) and may be
+ *   NULL / 0. */
+fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
+                                 const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                 const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                 float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode of one query against a contiguous K/V ([C] Summary: the single-decode
+ * entry point).  k and v are [dev] [kv_len, num_kv_heads, head_dim] with the
+ * same dtype rules as fi_batch_decode_paged; q and o are
+ * [num_qo_heads, head_dim]; lse is [num_qo_heads] or NULL. */
+fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const void* v, fi_dtype k_dtype,
+                           fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float k_scale, float v_scale, void* o, fi_dtype o_dtype, float* lse,
+                           float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Widen n fp8 codes into a 2-byte type with the same device conversion the
+ * attention kernels use (no scaling).  src in {E4M3, E5M2}, dst in {F16, BF16};
+ * codes [dev] [n] bytes, out [dev] [n] 2-byte values.  This makes the
+ * conversion testable code by code ([C] design notes: the vec_cast paragraph
+ * records a decoder with the wrong bias and broken denormals that no test
+ * could reach). */
+fi_status fi_fp8_widen(const uint8_t* codes, int64_t n, fi_dtype src, fi_dtype dst, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FI_H_ */

@@ -1,0 +1,227 @@
+"""C-ABI tests that need no GPU (CPU only).
+
+* libfi.so loads and exports every function include/fi.h declares.
+* Each refusal returns its status and a sentence naming the call, the
+  argument and the dtype(s), before any HIP call: the refusal set of "fp8 KV
+  cache in the in-tree prefill kernel" (AMD-Ecosystem/flashinfer PR #368,
+  Refusals and Test plan: fp8 query, integer KV, float32, mismatched k/v,
+  prefill 2-byte KV that differs from q) and of "Enable Hopper FA3 FP8
+  attention in decode.py" (flashinfer PR #2148, Walkthrough: fp8 output).
+
+Device pointers here are NULL (or, for checks that come after the NULL check,
+fake addresses), so these tests never reach a kernel; they are skipped where a
+GPU is visible, and the same refusals are exercised on the GPU with real
+tensors by test_gpu_decode.py.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from attention_paged_fp8_amd import fi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fi.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer refusal checks run only without a GPU")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fi.LIB_PATH):
+        from attention_paged_fp8_amd.build import build
+        build()
+    return fi.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:fi_status|size_t|const char\*)\s+(fi_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) == 6, names
+    assert sorted(fi.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fi.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), f"{n} not exported as a text symbol"
+
+
+def test_workspace_bound(L):
+    assert fi.fi_decode_workspace_bytes(0, 32, 128, 4096) == 0
+    # B * ceil(max_kv / 128) chunks * H_qo * (D + 1) floats
+    assert fi.fi_decode_workspace_bytes(64, 32, 128, 4096) == 64 * 32 * 32 * 129 * 4
+    assert fi.fi_decode_workspace_bytes(8, 64, 128, 131072) == 8 * 1024 * 64 * 129 * 4
+    assert fi.fi_decode_workspace_bytes(1, 4, 64, 1) == 1 * 2 * 4 * 65 * 4
+
+
+def _kv(k_dtype="e4m3", v_dtype=None, *, page=16, hkv=2, d=64, lens=(5, 17), ptrs=False, lpl=None):
+    """A paged-KV struct over host arrays; device pointers NULL unless ptrs."""
+    lens = np.asarray(lens)
+    npg = (lens + page - 1) // page
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    last = (lens - (npg - 1) * page).astype(np.int32) if lpl is None else np.asarray(lpl, np.int32)
+    s = fi.PagedKV()
+    fake = 0x10000 if ptrs else None
+    s.k = s.v = fake
+    s.k_dtype = fi.DTYPES[k_dtype]
+    s.v_dtype = fi.DTYPES[v_dtype or k_dtype]
+    s.stride_token = hkv * d
+    s.stride_head = d
+    s.stride_page = page * hkv * d
+    s.num_pages, s.page_size, s.num_kv_heads, s.head_dim = int(indptr[-1]), page, hkv, d
+    s.indptr = s.indices = s.last_page_len = fake
+    s.indptr_h = indptr.ctypes.data
+    s.last_page_len_h = last.ctypes.data
+    s.k_scale = s.v_scale = 1.0
+    return s, (indptr, last)
+
+
+def _decode(L, kv, q="f16", o="default", hq=4, batch=2, qp=None, op=None, ws=None, wsb=0, sm=0.0):
+    return L.fi_batch_decode_paged(qp, fi.DTYPES[q], batch, hq, ctypes.byref(kv), op, fi.DTYPES[o], None, sm, ws, wsb,
+                                   None)
+
+
+def _prefill(L, kv, q="f16", o="default", hq=4, batch=2, qp=None, op=None):
+    qo = np.array([0, 3, 7], np.int32)
+    return L.fi_batch_prefill_paged(qp, fi.DTYPES[q], None, qo.ctypes.data, batch, hq, ctypes.byref(kv), 1, op,
+                                    fi.DTYPES[o], None, 0.0, None, 0, None)
+
+
+def _single(L, q="f16", k="e4m3", v=None, o="default", d=64, hq=4, hkv=2, kv_len=8):
+    return L.fi_single_decode(None, fi.DTYPES[q], None, None, fi.DTYPES[k], fi.DTYPES[v or k], kv_len, hq, hkv, d,
+                              1.0, 1.0, None, fi.DTYPES[o], None, 0.0, None, 0, None)
+
+
+def _err(L):
+    return L.fi_last_error().decode()
+
+
+DTYPE_REFUSALS = [
+    # (call, kwargs, status, fragment)
+    ("decode", dict(q="e4m3"), 1, "fi_batch_decode_paged: q has dtype float8_e4m3fn; an fp8 query is not supported"),
+    ("decode", dict(q="f32"), 1, "q has dtype float32"),
+    ("decode", dict(o="e4m3"), 1, "o has dtype float8_e4m3fn; an fp8 output is not supported"),
+    ("decode", dict(o="e5m2"), 1, "an fp8 output is not supported"),
+    ("decode", dict(o="f32"), 1, "o has dtype float32"),
+    ("decode", dict(k="f16", v="bf16"), 1, "fi_batch_decode_paged: k has dtype float16 but v has dtype bfloat16"),
+    ("decode", dict(k="e4m3", v="e5m2"), 1, "k has dtype float8_e4m3fn but v has dtype float8_e5m2"),
+    ("decode", dict(k="e4m3", v="f16"), 1, "k has dtype float8_e4m3fn but v has dtype float16"),
+    ("decode", dict(k="i8"), 1, "KV cache has dtype int8, which has no float interpretation"),
+    ("decode", dict(k="u8"), 1, "KV cache has dtype uint8, which has no float interpretation"),
+    ("decode", dict(k="f32"), 1, "KV cache has dtype float32"),
+    ("decode", dict(k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant"),
+    ("decode", dict(k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
+    ("prefill", dict(q="f16", k="bf16"), 1,
+     "fi_batch_prefill_paged: q has dtype float16 but the KV cache has dtype bfloat16; prefill needs a 2-byte KV"),
+    ("prefill", dict(q="bf16", k="f16"), 1, "q has dtype bfloat16 but the KV cache has dtype float16"),
+    ("prefill", dict(q="e5m2"), 1, "an fp8 query is not supported"),
+    ("prefill", dict(k="f16", v="bf16"), 1, "k has dtype float16 but v has dtype bfloat16"),
+    ("prefill", dict(k="i8"), 1, "no float interpretation"),
+    ("prefill", dict(o="e4m3"), 1, "an fp8 output is not supported"),
+    ("single", dict(k="f16", v="bf16"), 1, "fi_single_decode: k has dtype float16 but v has dtype bfloat16"),
+    ("single", dict(k="u8"), 1, "fi_single_decode: KV cache has dtype uint8"),
+    ("single", dict(o="e4m3"), 1, "fi_single_decode: o has dtype float8_e4m3fn"),
+    ("single", dict(q="e4m3"), 1, "fi_single_decode: q has dtype float8_e4m3fn"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("call,kw,status,frag", DTYPE_REFUSALS, ids=[f"{c}-{i}" for i, (c, *_r) in enumerate(DTYPE_REFUSALS)])
+def test_dtype_refusals(L, call, kw, status, frag):
+    k = kw.get("k", "e4m3")
+    v = kw.get("v", k)
+    q = kw.get("q", "f16")
+    o = kw.get("o", "default")
+    if call == "single":
+        st = _single(L, q=q, k=k, v=v, o=o)
+    else:
+        kv, keep = _kv(k, v)
+        st = _decode(L, kv, q=q, o=o) if call == "decode" else _prefill(L, kv, q=q, o=o)
+    assert st == status
+    assert frag in _err(L), _err(L)
+
+
+@no_gpu
+def test_decode_accepts_mixed_2byte_before_pointer_checks(L):
+    """Decode admits a 2-byte KV that differs from q ("fp8 KV cache in the
+    in-tree prefill kernel", Architecture / design notes): with NULL pointers
+    the first refusal is the pointer check, not a dtype refusal."""
+    for q, k in (("f16", "bf16"), ("bf16", "f16")):
+        kv, keep = _kv(k)
+        st = _decode(L, kv, q=q)
+        assert st == 3 and "must not be NULL" in _err(L), _err(L)
+
+
+@no_gpu
+def test_order_dtype_before_shape(L):
+    kv, keep = _kv("i8", d=96)  # both an int8 KV and a bad head_dim: dtype is reported
+    assert _decode(L, kv) == 1 and "int8" in _err(L)
+
+
+@no_gpu
+@pytest.mark.parametrize("case", ["head_dim", "heads_ratio", "page_size", "batch"])
+def test_shape_refusals(L, case):
+    if case == "head_dim":
+        kv, keep = _kv(d=96)
+        st, frag = _decode(L, kv), "head_dim=96"
+    elif case == "heads_ratio":
+        kv, keep = _kv(hkv=3)
+        st, frag = _decode(L, kv, hq=4), "num_qo_heads=4 is not a multiple of num_kv_heads=3"
+    elif case == "page_size":
+        kv, keep = _kv(page=16)
+        kv.page_size = 12
+        st, frag = _decode(L, kv, qp=0x10000, op=0x10000), "page_size=12"
+    else:
+        kv, keep = _kv()
+        st, frag = _decode(L, kv, batch=-1), "batch=-1 is outside"
+    assert st == 2, _err(L)
+    assert frag in _err(L)
+
+
+@no_gpu
+def test_argument_refusals(L):
+    kv, keep = _kv(ptrs=True)
+    assert _decode(L, kv, qp=0x10008, op=0x10000) == 3 and "16-byte aligned" in _err(L)
+    kv2, keep2 = _kv(ptrs=True, lpl=[5, 0])
+    assert _decode(L, kv2, qp=0x10000, op=0x10000) == 3 and "last_page_len[1]=0" in _err(L)
+    kv3, keep3 = _kv(ptrs=True, lpl=[17, 1])
+    assert _decode(L, kv3, qp=0x10000, op=0x10000) == 3 and "last_page_len[0]=17" in _err(L)
+    kv4, keep4 = _kv(ptrs=True)
+    kv4.k_scale = float("nan")
+    assert _decode(L, kv4, qp=0x10000, op=0x10000) == 3 and "k_scale" in _err(L)
+    kv5, keep5 = _kv(ptrs=True)
+    kv5.v_scale = 0.0
+    assert _decode(L, kv5, qp=0x10000, op=0x10000) == 3 and "v_scale" in _err(L)
+    kv6, keep6 = _kv(ptrs=True)
+    kv6.stride_token = 2 * 64 + 4  # fp8 rows no longer 16-byte aligned
+    assert _decode(L, kv6, qp=0x10000, op=0x10000) == 3 and "16-byte aligned rows" in _err(L)
+
+
+@no_gpu
+def test_workspace_too_small(L, monkeypatch):
+    monkeypatch.setenv("FI_SPLIT_KV", "128")
+    kv, keep = _kv(ptrs=True, lens=(1000, 300))
+    st = _decode(L, kv, qp=0x10000, op=0x10000, ws=0x10000, wsb=16)
+    assert st == 4 and "workspace_bytes=16" in _err(L), _err(L)
+
+
+@no_gpu
+def test_widen_refusals(L):
+    assert L.fi_fp8_widen(None, 4, fi.DTYPES["f16"], fi.DTYPES["f16"], None, None) == 1
+    assert "src has dtype float16" in _err(L)
+    assert L.fi_fp8_widen(None, 4, fi.DTYPES["e4m3"], fi.DTYPES["e4m3"], None, None) == 1
+    assert L.fi_fp8_widen(None, 4, fi.DTYPES["e4m3"], fi.DTYPES["bf16"], None, None) == 3
+    assert L.fi_fp8_widen(None, 0, fi.DTYPES["e4m3"], fi.DTYPES["bf16"], None, None) == 0
+
+
+def test_python_error_classes():
+    assert issubclass(fi.FiValueError, ValueError)
+    assert issubclass(fi.FiRuntimeError, RuntimeError)

@@ -1,0 +1,272 @@
+"""GPU parity tests for decode (batched paged, single) and the fp8 widening,
+through the C ABI, against the float64 oracle.
+
+Cases: every fp8 code widened bitwise; the measured configurations 1, 2, 4 and
+5 compared element by element at full size; a matrix of small shapes spanning
+several 32-token blocks, ragged tails, empty and one-token requests, page
+sizes 1..128, head_dim 64 and 128, GQA groups 1..32, all q / KV / o dtype
+combinations decode admits, forced split-KV; and the invariants: run-to-run
+bitwise determinism, bitwise page-permutation invariance, an fp8 run equal
+bitwise to a run on the same values pre-widened to q's type (the equivalence
+design of "fp8 KV cache in the in-tree prefill kernel", Test plan), the
+k_scale fold, constant V, NaN-poisoned padding and unreferenced pages, and a
+non-default (head-major) pool layout.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+from oracle.fp8 import fp8_table
+from attention_paged_fp8_amd import fi
+from workloads import make_config, make_paged
+from gpu_util import (O_TOL, T2, assert_parity, dev_2byte, paged_kv, run_decode, say, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ fp8 codes
+@pytest.mark.parametrize("src", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dst", ["f16", "bf16"])
+def test_fp8_widen_all_codes_bitwise(gpu_device, src, dst):
+    say("widen", src, dst)
+    codes = torch.arange(256, dtype=torch.uint8, device=gpu_device).repeat(3)  # 768 codes, ragged-free and reused
+    codes = torch.cat([codes, codes[:5]])  # a ragged tail of 5
+    out = torch.empty(codes.numel(), dtype=T2[dst], device=gpu_device)
+    fi.fi_fp8_widen(codes, src, out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    ref = fp8_table(src)[codes.cpu().numpy()]
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 stays -0
+
+
+# ------------------------------------------------------------------ config 1
+def test_config1_single_and_batch(gpu_device):
+    say("config1")
+    w = make_config(1)
+    d = upload(w, gpu_device)
+    o_ref, l_ref = OA.batch_decode(w)
+    o_b, l_b, _ = run_decode(w, d)
+    assert_parity(o_b, l_b, o_ref, l_ref, "f16", "batch decode")
+    # single decode: contiguous K/V [kv_len, H, D] (pages are contiguous in config 1)
+    kv_len = int(w["kv_lens"][0])
+    k = d["k"].reshape(-1, w["num_kv_heads"], w["head_dim"])[:kv_len]
+    v = d["v"].reshape(-1, w["num_kv_heads"], w["head_dim"])[:kv_len]
+    o = torch.full((w["num_qo_heads"], w["head_dim"]), float("nan"), dtype=torch.float16, device=gpu_device)
+    lse = torch.empty(w["num_qo_heads"], dtype=torch.float32, device=gpu_device)
+    fi.fi_single_decode(d["q"][0], k, v, o, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype="e4m3", lse=lse)
+    torch.cuda.synchronize()
+    o_s = o.double().cpu().numpy()
+    assert_parity(o_s[None], lse.double().cpu().numpy()[None], o_ref, l_ref, "f16", "single decode")
+    # the oracle's contiguous single-decode definition agrees, and the two entry points agree bitwise
+    o_r2, l_r2 = OA.single_decode(w["q"][0], "f16", w["k_pool"].reshape(-1, 4, 64)[:kv_len],
+                                  w["v_pool"].reshape(-1, 4, 64)[:kv_len], "e4m3", w["k_scale"], w["v_scale"])
+    assert np.allclose(o_r2, o_ref[0], atol=1e-12)
+    assert np.array_equal(o_s, o_b[0])
+
+
+# ------------------------------------------------------------------ small matrix
+SMALL = [
+    # (kvd, q, o, page, d, hq, hkv, lens, split)
+    ("e4m3", "f16", "f16", 16, 128, 32, 8, (1, 31, 32, 33, 200, 517, 0, 64), None),
+    ("e4m3", "bf16", "bf16", 16, 128, 32, 8, (700, 129, 5), "128"),
+    ("e5m2", "bf16", "bf16", 64, 128, 64, 8, (1000, 3, 2049), "256"),
+    ("e5m2", "f16", "bf16", 4, 64, 8, 2, (77, 300, 1), None),
+    ("e4m3", "bf16", "f16", 1, 64, 4, 4, (9, 40, 130), "128"),
+    ("e4m3", "f16", "f16", 128, 128, 32, 1, (1500, 260), "128"),   # group 32: two 16-row slices
+    ("e4m3", "f16", "f16", 32, 128, 12, 4, (100, 333), None),        # group 3
+    ("f16", "f16", "f16", 16, 128, 32, 8, (400, 65, 1), "128"),
+    ("bf16", "bf16", "bf16", 16, 64, 16, 2, (257, 31), None),
+    ("bf16", "f16", "f16", 16, 128, 32, 8, (600, 90), "128"),        # mixed 2-byte decode
+    ("f16", "bf16", "bf16", 8, 128, 8, 8, (300, 12), None),          # mixed the other way
+    ("e5m2", "f16", "f16", 2, 128, 16, 16, (55, 1, 0, 1024), "128"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-q{c[1]}-o{c[2]}-p{c[3]}-d{c[4]}-h{c[5]}x{c[6]}-s{c[8]}" for c in SMALL])
+def test_decode_small(gpu_device, case):
+    kvd, q, o, page, d, hq, hkv, lens, split = case
+    say("decode small", case)
+    w = make_paged(11, kv_lens=list(lens), hq=hq, hkv=hkv, d=d, page=page, q=q, kvd=kvd, o=o, extra_pages=3)
+    dv = upload(w, gpu_device)
+    o_ref, l_ref = OA.batch_decode(w)
+    og, lg, _ = run_decode(w, dv, split=split)
+    assert_parity(og, lg, o_ref, l_ref, o, str(case))
+    # empty requests: o = 0, lse = -inf
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert np.all(og[i] == 0) and np.all(np.isneginf(lg[i]))
+
+
+# ------------------------------------------------------------------ full-size configs
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_config_full_size(gpu_device, cfg):
+    say("config", cfg)
+    w = make_config(cfg)
+    d = upload(w, gpu_device)
+    og, lg, _ = run_decode(w, d)
+    del d
+    torch.cuda.empty_cache()
+    o_ref, l_ref = OA.batch_decode(w)
+    err = assert_parity(og, lg, o_ref, l_ref, w["o_dtype"], f"config {cfg}")
+    print(f"config {cfg}: max |o - oracle| = {err:.3e}")
+
+
+@pytest.mark.parametrize("kvd", ["f16", "bf16", "e4m3"])
+def test_config5_legs(gpu_device, kvd):
+    say("config5", kvd)
+    w = make_config(5, kvd=kvd)
+    d = upload(w, gpu_device)
+    og, lg, _ = run_decode(w, d)
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(og, lg, o_ref, l_ref, "f16", f"config 5 {kvd}")
+
+
+def test_config5_refusals_with_real_tensors(gpu_device):
+    """k/v dtype mismatch, integer KV and fp8 output must error, and leave o
+    untouched."""
+    say("config5 refusals")
+    w = make_paged(5, kv_lens=[100, 40], hq=32, hkv=8, d=128, page=16, q="f16", kvd="e4m3")
+    d = upload(w, gpu_device)
+    o = torch.full((2, 32, 128), 7.0, dtype=torch.float16, device=gpu_device)
+    cases = [
+        (dict(k_dtype="e4m3", v_dtype="e5m2"), "k has dtype float8_e4m3fn but v has dtype float8_e5m2"),
+        (dict(kv_dtype="i8"), "KV cache has dtype int8, which has no float interpretation"),
+        (dict(kv_dtype="u8"), "KV cache has dtype uint8"),
+    ]
+    for kw, frag in cases:
+        kv, keep = fi.make_paged_kv(d["k"], d["v"], d["indptr"], d["indices"], d["lpl"], k_scale=w["k_scale"],
+                                    v_scale=w["v_scale"], indptr_h=w["indptr"], last_page_len_h=w["last_page_len"], **kw)
+        with pytest.raises(fi.FiValueError, match=frag):
+            fi.fi_batch_decode_paged(d["q"], kv, o)
+    kv, keep = paged_kv(w, d)
+    with pytest.raises(fi.FiValueError, match="an fp8 output is not supported"):
+        fi.fi_batch_decode_paged(d["q"], kv, o, o_dtype="e4m3")
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0)
+    # prefill refuses a bf16 cache under an f16 query; decode accepts it (tested above)
+    w2 = make_paged(6, qo_lens=[4], prefix_lens=[10], hq=32, hkv=8, d=128, page=16, q="f16", kvd="bf16")
+    d2 = upload(w2, gpu_device)
+    kv2, keep2 = paged_kv(w2, d2)
+    o2 = torch.full((4, 32, 128), 7.0, dtype=torch.float16, device=gpu_device)
+    with pytest.raises(fi.FiValueError, match="prefill needs a 2-byte KV cache of the query's dtype"):
+        fi.fi_batch_prefill_paged(d2["q"], d2["qo_indptr"], kv2, o2, qo_indptr_h=w2["qo_indptr"])
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 7.0)
+
+
+# ------------------------------------------------------------------ invariants
+def _mid_workload(seed=21, kvd="e4m3", q="bf16", extra_pages=0):
+    return make_paged(seed, kv_lens=[1500, 33, 900, 2048, 7, 640], hq=32, hkv=8, d=128, page=16, q=q, kvd=kvd,
+                      extra_pages=extra_pages)
+
+
+def test_determinism_and_page_permutation(gpu_device):
+    say("determinism + page permutation")
+    w = _mid_workload()
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_decode(w, d, split="256")
+    o2, l2, _ = run_decode(w, d, split="256")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # move every page elsewhere in the pool and remap the indices
+    P = w["k_pool"].shape[0]
+    perm = np.random.default_rng(3).permutation(P)
+    inv = np.argsort(perm)
+    w2 = dict(w, k_pool=w["k_pool"][perm], v_pool=w["v_pool"][perm], indices=inv[w["indices"]].astype(np.int32))
+    d2 = upload(w2, gpu_device)
+    o3, l3, _ = run_decode(w2, d2, split="256")
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+@pytest.mark.parametrize("kvd,q", [("e4m3", "bf16"), ("e5m2", "f16")])
+def test_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
+    """fp8 K/V give bit-identical output to the same values stored widened in
+    q's 2-byte type, with the same scales."""
+    say("prewidened", kvd, q)
+    w = _mid_workload(kvd=kvd, q=q)
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_decode(w, d)
+    tab = fp8_table(kvd)
+    kw = tab[w["k_pool"]].astype(np.float32)
+    vw = tab[w["v_pool"]].astype(np.float32)
+    kw[~np.isfinite(kw)] = np.nan
+    k2 = torch.from_numpy(kw).to(T2[q]).to(gpu_device)
+    v2 = torch.from_numpy(vw).to(T2[q]).to(gpu_device)
+    kv, keep = paged_kv(w, d, k=k2, v=v2, kv_dtype=q)
+    o2, l2, _ = run_decode(w, d, kv=kv)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_kscale_fold(gpu_device):
+    """Scaling k_scale by c equals scaling sm_scale by c; dropping the fold
+    would fail the oracle comparison (the A/B check recorded in "fp8 KV cache in
+    the in-tree prefill kernel", Test plan)."""
+    say("k_scale fold")
+    w = _mid_workload(q="f16")
+    d = upload(w, gpu_device)
+    c = 4.0
+    sm = 0.05
+    kv_a, ka = paged_kv(w, d, k_scale=w["k_scale"] * c)
+    oa, la, _ = run_decode(w, d, kv=kv_a, sm_scale=sm, o_dtype="f16")
+    kv_b, kb = paged_kv(w, d)
+    ob, lb, _ = run_decode(w, d, kv=kv_b, sm_scale=sm * c, o_dtype="f16")
+    assert np.max(np.abs(oa - ob)) <= 2e-3 and np.max(np.abs(la - lb)) <= 1e-4
+    w_ref = dict(w, k_scale=w["k_scale"] * c)
+    o_ref, l_ref = OA.batch_decode(w_ref, sm_scale=sm)
+    assert_parity(oa, la, o_ref, l_ref, "f16", "k_scale fold")
+    o_wrong, _ = OA.batch_decode(w, sm_scale=sm)  # the fold left out
+    assert np.max(np.abs(oa - o_wrong)) > O_TOL["f16"]
+
+
+def test_constant_v(gpu_device):
+    """Every token carries the same V row: the output is that row times v_scale
+    (up to the output rounding)."""
+    say("constant V")
+    w = _mid_workload(q="f16")
+    row = w["v_pool"][w["indices"][0], 0].copy()
+    w["v_pool"][:] = row
+    d = upload(w, gpu_device)
+    o, l, _ = run_decode(w, d, split="256", o_dtype="f16")
+    target = fp8_table("e4m3")[row] * w["v_scale"]  # [H_kv, D]
+    grp = 32 // 8
+    exp = np.repeat(target, grp, axis=0)[None].repeat(o.shape[0], 0)
+    np.testing.assert_allclose(o, exp.astype(np.float16).astype(np.float64), rtol=2e-3, atol=1e-6)
+
+
+def test_poisoned_pages_stay_finite(gpu_device):
+    """Unused slots and unreferenced pages hold NaN codes; outputs stay finite."""
+    say("poisoned pages")
+    w = _mid_workload(extra_pages=50)
+    assert np.isnan(fp8_table("e4m3")[w["k_pool"][~w["valid"]]]).all()
+    d = upload(w, gpu_device)
+    o, l, _ = run_decode(w, d, split="128")
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(o, l, o_ref, l_ref, "bf16", "poisoned")
+
+
+def test_head_major_pool_layout(gpu_device):
+    """A pool stored [num_pages, H_kv, page_size, D] passed through its strides."""
+    say("HND layout")
+    w = _mid_workload(q="f16")
+    d = upload(w, gpu_device)
+    k_hnd = d["k"].permute(0, 2, 1, 3).contiguous()  # [P, H, page, D]
+    v_hnd = d["v"].permute(0, 2, 1, 3).contiguous()
+    kv, keep = paged_kv(w, d, k=k_hnd.permute(0, 2, 1, 3), v=v_hnd.permute(0, 2, 1, 3))
+    o, l, _ = run_decode(w, d, kv=kv)
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(o, l, o_ref, l_ref, "f16", "HND")
+
+
+def test_split_and_unsplit_agree(gpu_device):
+    say("split vs unsplit")
+    w = _mid_workload()
+    d = upload(w, gpu_device)
+    o_ref, l_ref = OA.batch_decode(w)
+    for split in ("off", "128", "384", "auto"):
+        o, l, _ = run_decode(w, d, split=split)
+        assert_parity(o, l, o_ref, l_ref, "bf16", f"split={split}")
+    o, l, _ = run_decode(w, d, workspace=False)
+    assert_parity(o, l, o_ref, l_ref, "bf16", "no workspace")

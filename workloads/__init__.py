@@ -100,7 +100,8 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
     a batch size (lengths are then drawn first, as described above).
 
     Decode: ``kv_lens`` (qo_len = 1 per request).  Prefill: ``qo_lens`` and
-    ``prefix_lens`` (kv_len = qo_len + prefix_len)."""
+    ``prefix_lens`` (kv_len = qo_len + prefix_len), or ``qo_lens`` and
+    ``kv_lens`` directly."""
     rng = np.random.default_rng(seed)
     if kv_range is not None:
         kv_lens = rng.integers(kv_range[0], kv_range[1] + 1, size=batch)
@@ -112,8 +113,11 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
         qo_lens = np.ones_like(kv_lens)
     else:
         qo_lens = np.asarray(qo_lens, dtype=np.int64)
-        prefix_lens = np.zeros_like(qo_lens) if prefix_lens is None else np.asarray(prefix_lens, dtype=np.int64)
-        kv_lens = qo_lens + prefix_lens
+        if kv_lens is not None and prefix_lens is None:
+            kv_lens = np.asarray(kv_lens, dtype=np.int64)  # explicit, may be shorter than qo_lens
+        else:
+            prefix_lens = np.zeros_like(qo_lens) if prefix_lens is None else np.asarray(prefix_lens, dtype=np.int64)
+            kv_lens = qo_lens + prefix_lens
     B = len(kv_lens)
     npages = (kv_lens + page - 1) // page
     indptr = np.zeros(B + 1, dtype=np.int32)
