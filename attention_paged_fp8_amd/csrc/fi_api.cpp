@@ -157,11 +157,19 @@ fi_status check_paged(const char* fn, int32_t batch, const fi_paged_kv* kv, int6
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-constexpr int kMinAutoChunk = 256;   // smallest chunk the workspace bound allows for
-constexpr int kTargetWorkgroups = 2048;
+#ifndef FI_DECODE_MIN_CHUNK
+#define FI_DECODE_MIN_CHUNK 256
+#endif
+#ifndef FI_DECODE_TARGET_WG
+#define FI_DECODE_TARGET_WG 2048
+#endif
+constexpr int kMinAutoChunk = FI_DECODE_MIN_CHUNK;  // smallest chunk the planner picks by itself
+constexpr int kTargetWorkgroups = FI_DECODE_TARGET_WG;  // workgroups the planner aims for
 
-// Split-KV plan: tokens per chunk.  0 split => chunk covers the longest request.
-int64_t plan_chunk(int64_t max_kv, int64_t total_kv, int64_t units_per_token, bool have_ws) {
+// Split-KV plan: tokens per chunk (a multiple of kChunkQuantum); a chunk that
+// covers the longest request means no split.  `groups` workgroups share each
+// token (kv head groups x row-slice groups).
+int64_t plan_chunk(int64_t max_kv, int64_t total_kv, int64_t groups, bool have_ws) {
   const int64_t q = fi::kChunkQuantum;
   const int64_t whole = std::max<int64_t>(q, round_up(std::max<int64_t>(max_kv, 1), q));
   if (!have_ws) return whole;
@@ -171,7 +179,7 @@ int64_t plan_chunk(int64_t max_kv, int64_t total_kv, int64_t units_per_token, bo
     const long n = std::strtol(env, nullptr, 10);
     if (n > 0) return std::min(whole, std::max<int64_t>(q, round_up(n, q)));
   }
-  const int64_t work = total_kv * units_per_token;
+  const int64_t work = total_kv * groups;
   int64_t c = round_up(std::max<int64_t>(1, ceil_div(work, kTargetWorkgroups)), q);
   c = std::max<int64_t>(c, kMinAutoChunk);
   return std::min(c, whole);
@@ -183,44 +191,108 @@ size_t partial_bytes(int64_t batch, int64_t max_chunks, int64_t hqo, int64_t d) 
 }
 
 fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_dtype kv_dtype, fi_dtype o_dtype,
-                     int32_t batch, int32_t head_dim, int64_t max_kv, int64_t total_kv, void* workspace,
-                     size_t workspace_bytes, float sm_scale, float k_scale, float v_scale, hipStream_t stream) {
+                     int32_t batch, int32_t head_dim, const int32_t* indptr_h, const int32_t* last_page_len_h,
+                     int32_t page_size, int64_t max_kv, int64_t total_kv, void* workspace, size_t workspace_bytes,
+                     float sm_scale, float k_scale, float v_scale, hipStream_t stream) {
+  // Workgroup shape: up to 4 waves, one per (kv head, 16-row slice of its GQA
+  // group); the heads of a workgroup are adjacent, so each token's rows of
+  // those heads are read as one contiguous run.
   const int nsub = (p.group + fi::kDecodeRows - 1) / fi::kDecodeRows;
   p.nsub = nsub;
-  const int64_t chunk = plan_chunk(max_kv, total_kv, (int64_t)p.num_kv_heads * nsub, workspace != nullptr);
-  const int64_t max_chunks = std::max<int64_t>(1, ceil_div(max_kv, chunk));
-  const size_t need = partial_bytes(batch, max_chunks, p.num_qo_heads, head_dim);
+  p.spw = nsub <= fi::kDecodeWaves ? nsub : fi::kDecodeWaves;
+  const int max_hpw = fi::kDecodeWaves / p.spw;  // 4, 2 or 1
+  int hpw_shift = 0;
+  while (hpw_shift < 2 && (2 << hpw_shift) <= max_hpw && p.num_kv_heads % (2 << hpw_shift) == 0) ++hpw_shift;
+  p.hpw_shift = hpw_shift;
+  p.n_hgroups = p.num_kv_heads >> hpw_shift;
+  p.n_sgroups = (nsub + p.spw - 1) / p.spw;
+  const int64_t groups = (int64_t)p.n_hgroups * p.n_sgroups;
+  p.batch = batch;
+
+  // kv length of request i from the host copy of the page table
+  auto kv_of = [&](int i) -> int64_t {
+    if (!indptr_h) return total_kv;
+    const int32_t np = indptr_h[i + 1] - indptr_h[i];
+    return np > 0 ? (int64_t)(np - 1) * page_size + last_page_len_h[i] : 0;
+  };
+  const char* env = std::getenv("FI_SPLIT_KV");
+  const bool forced = env && *env && std::strcmp(env, "auto") != 0;
+  bool merge = false;
+  bool empty_any = false;
+  for (int32_t i = 0; i < batch; ++i) empty_any |= (kv_of(i) == 0);
+
+  // Balanced split: equal slices of the (group, request, token) space, one per
+  // workgroup slot of the device (the default whenever a workspace is given).
+  p.balanced = 0;
+  if (workspace && !forced && batch <= fi::kBalancedMaxBatch && total_kv > 0) {
+    const int slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
+    if (slots > 0) {
+      const int64_t W = total_kv * groups;
+      int64_t slice = round_up(ceil_div(W, slots), fi::kDecodeStep);
+      slice = std::max<int64_t>(slice, fi::kChunkQuantum);
+      p.balanced = 1;
+      p.slice = slice;
+      p.n_wg = (int32_t)ceil_div(W, slice);
+      p.max_chunks = (int32_t)(ceil_div(std::max<int64_t>(max_kv, 1), slice) + 1);
+      p.chunk = 0;
+      // a merge is needed if some (request, group) segment spans several slices
+      int64_t pre = 0;
+      for (int32_t i = 0; i < batch && !merge; ++i) {
+        const int64_t len = kv_of(i);
+        for (int64_t gi = 0; gi < groups && len > 0; ++gi) {
+          const int64_t s0 = gi * total_kv + pre, s1 = s0 + len;
+          if (s0 / slice != (s1 - 1) / slice) {
+            merge = true;
+            break;
+          }
+        }
+        pre += len;
+      }
+      merge |= empty_any;  // the merge kernel also writes requests without keys
+    }
+  }
+  if (!p.balanced) {
+    const int64_t chunk = plan_chunk(max_kv, total_kv, groups, workspace != nullptr);
+    const int64_t max_chunks = std::max<int64_t>(1, ceil_div(max_kv, chunk));
+    if (max_chunks * groups * (int64_t)batch > 0x7fffffff)
+      return fail(FI_E_SHAPE, fn, "the split needs more than 2^31 workgroups");
+    p.chunk = (int32_t)chunk;
+    p.max_chunks = (int32_t)max_chunks;
+    merge = max_chunks > 1;
+  }
+  const size_t need = merge ? partial_bytes(batch, p.max_chunks, p.num_qo_heads, head_dim) + (size_t)batch * groups * 4 : 0;
   if (need > 0 && workspace_bytes < need)
     return fail(FI_E_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the %zu bytes this split needs "
                 "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
   if (need > 0 && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
-  if (max_chunks > 0x7fffffff) return fail(FI_E_SHAPE, fn, "too many chunks");
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
-  if (max_chunks * p.num_kv_heads * nsub * (int64_t)batch > 0x7fffffff)
-    return fail(FI_E_SHAPE, fn, "the split needs more than 2^31 workgroups");
-  p.chunk = (int32_t)chunk;
-  p.max_chunks = (int32_t)max_chunks;
-  p.batch = batch;
   p.scale_log2 = scale * k_scale * fi::kLog2eHost;
   p.v_scale = v_scale;
-  p.part_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
-  p.part_lse = need ? reinterpret_cast<float*>(workspace) + (size_t)batch * max_chunks * p.num_qo_heads * head_dim
-                    : nullptr;
+  float* ws = reinterpret_cast<float*>(workspace);
+  const size_t npart = (size_t)batch * p.num_qo_heads * p.max_chunks;
+  p.part_o = need ? ws : nullptr;
+  p.part_lse = need ? ws + npart * head_dim : nullptr;
+  p.nch = need ? reinterpret_cast<int32_t*>(ws + npart * (head_dim + 1)) : nullptr;
   if (batch == 0) return FI_OK;
   hipError_t err = fi::launch_decode(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, stream);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(err));
-  if (max_chunks > 1) {
+  if (merge) {
     fi::MergeParams mp{};
     mp.o = p.o;
     mp.lse = p.lse;
     mp.part_o = p.part_o;
     mp.part_lse = p.part_lse;
+    mp.nch = p.nch;
     mp.indptr = p.indptr;
     mp.last_page_len = p.last_page_len;
     mp.page_size = p.page_size;
     mp.single_kv_len = p.single_kv_len;
     mp.num_qo_heads = p.num_qo_heads;
-    mp.chunk = p.chunk;
+    mp.group = p.group;
+    mp.hpw_shift = p.hpw_shift;
+    mp.spw = p.spw;
+    mp.n_hgroups = p.n_hgroups;
+    mp.n_sgroups = p.n_sgroups;
     mp.max_chunks = p.max_chunks;
     mp.v_scale = v_scale;
     err = fi::launch_merge(mp, o_dtype, head_dim, batch, stream);
@@ -237,9 +309,10 @@ const char* fi_last_error(void) { return g_err.c_str(); }
 
 size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_kv_len) {
   if (batch <= 0 || num_qo_heads <= 0 || head_dim <= 0 || max_kv_len <= 0) return 0;
-  // any plan, including a forced FI_SPLIT_KV chunk, uses chunks of at least kChunkQuantum tokens
-  const int64_t max_chunks = ceil_div(max_kv_len, fi::kChunkQuantum);
-  return partial_bytes(batch, std::max<int64_t>(max_chunks, 2), num_qo_heads, head_dim);
+  // every plan uses pieces of at least kChunkQuantum tokens; a balanced slice
+  // boundary can add one more piece to a request
+  const int64_t max_chunks = ceil_div(max_kv_len, fi::kChunkQuantum) + 1;
+  return partial_bytes(batch, max_chunks, num_qo_heads, head_dim) + (size_t)batch * num_qo_heads * 4;
 }
 
 fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
@@ -277,8 +350,9 @@ fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, 
   p.num_qo_heads = num_qo_heads;
   p.num_kv_heads = kv->num_kv_heads;
   p.group = num_qo_heads / kv->num_kv_heads;
-  return run_decode(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, kv->head_dim, max_kv, total_kv, workspace,
-                    workspace_bytes, sm_scale, kv->k_scale, kv->v_scale, reinterpret_cast<hipStream_t>(stream));
+  return run_decode(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, kv->head_dim, kv->indptr_h, kv->last_page_len_h,
+                    kv->page_size, max_kv, total_kv, workspace, workspace_bytes, sm_scale, kv->k_scale, kv->v_scale,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const void* v, fi_dtype k_dtype,
@@ -314,8 +388,8 @@ fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const
   p.num_qo_heads = num_qo_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_qo_heads / num_kv_heads;
-  return run_decode(fn, p, q_dtype, k_dtype, o_dtype, 1, head_dim, kv_len, kv_len, workspace, workspace_bytes,
-                    sm_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
+  return run_decode(fn, p, q_dtype, k_dtype, o_dtype, 1, head_dim, nullptr, nullptr, 1 << 30, kv_len, kv_len,
+                    workspace, workspace_bytes, sm_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,

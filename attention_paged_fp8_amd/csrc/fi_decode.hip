@@ -8,40 +8,48 @@
 // "Enable Hopper FA3 FP8 attention in decode.py", flashinfer PR #2148:
 // plan()/run() arguments and split-KV knobs).
 //
-// Mapping onto the hardware.  A workgroup of 4 waves owns one (request, kv
-// head, 16-row slice of the GQA group, chunk of C tokens).  Each wave walks
-// 32-token blocks of the chunk (blocks w, w+4, ...):
-//   * each lane fetches, for two tokens of the block, a DL = head_dim/4
-//     element slice of the K and V rows (16-byte loads), straight from the
-//     page the token lives on;
-//   * K is widened in registers and multiplied on MFMA 16x16x32 as
-//     S^T = K * Q^T: the group's q rows (padded to 16) are the N dimension, the
-//     block's tokens the M dimension; both operands see the same permutation of
-//     head_dim, so no data movement is needed for QK;
-//   * V goes through a small per-wave LDS tile in its stored format; one
-//     transposed LDS read (ds_read_b64_tr_b8 for fp8, two tr_b16 for 2-byte)
-//     gives each lane one column over the eight tokens its P^T operand holds,
-//     so that O^T += V^T * P^T runs on the same MFMA shape with the
-//     probabilities taken directly from the S^T accumulator registers;
+// Mapping onto the hardware.  A workgroup of 4 waves owns one (request, chunk
+// of C tokens, group of adjacent kv heads); each wave owns one (kv head,
+// 16-row slice of its GQA group).  The chunk is walked in 16-token steps:
+//   * the whole workgroup loads the step's rows of its heads -- for fp8 K/V
+//     and head_dim 128, 4 heads x 128 B = 512 contiguous bytes per token and
+//     pool, the access pattern that measured closest to whole-page streaming
+//     on MI355X -- with 16-byte loads, two steps ahead, and stores them into an
+//     LDS stage whose 16-byte chunks are XOR-swizzled by row;
+//   * each wave reads its head's K rows from LDS (conflict-free 16-byte reads),
+//     widens fp8 in registers and multiplies on MFMA 16x16x32 as
+//     S^T = K * Q^T: the group's q rows (padded to 16) are the N dimension,
+//     the step's tokens the M dimension, and Q^T and K use the same
+//     permutation of head_dim;
+//   * the probabilities of the S^T accumulators are exactly the P^T operand of
+//     MFMA 16x16x16, so O^T += V^T * P^T needs V column-wise: one transposed
+//     LDS read (ds_read_b64_tr_b8) yields a lane's 4-token column of two
+//     16-wide head_dim blocks at once (tr_b16 for 2-byte V);
 //   * the MFMA type is bf16 when q or a 2-byte cache is bf16, else fp16; an
 //     fp16 operand meeting a bf16 one (mixed 2-byte decode) is split exactly
 //     into two bf16 MFMA operands, so no value is rounded;
 //   * the online softmax keeps a running max per row in base 2 (the logit
 //     scale sm_scale * k_scale * log2(e) folded into one multiply) and two
 //     sums: of the fp32 probabilities, for the log-sum-exp, and of the
-//     probabilities after rounding to q's type, which are the weights the PV
-//     MFMA applies, to normalise the output (so a constant V comes out
+//     probabilities after rounding to the MFMA type, which are the weights the
+//     PV MFMA applies, to normalise the output (so a constant V comes out
 //     unchanged).
-// The four waves' states are merged through LDS; the result is either the
-// final output (v_scale applied before the single rounding) or, when the
-// request is split into several chunks, an fp32 partial (output, log-sum-exp)
-// merged by merge_kernel.
+// Each wave writes either its rows' final output (v_scale applied before the
+// single rounding) or, when the request is split into several chunks, an fp32
+// partial (output, log-sum-exp) that merge_kernel combines.
+#include <atomic>
+
 #include "fi_device.hpp"
 
 namespace fi {
 
 // Page ids staged in LDS per window; a window spans kPidWindow pages.
 constexpr int kPidWindow = 1024;
+
+// Workgroups per CU the register allocation is sized for (4 waves each).
+#ifndef FI_DECODE_MIN_WG_PER_CU
+#define FI_DECODE_MIN_WG_PER_CU 3
+#endif
 
 template <bool QBF16, int KVF, bool OBF16, int D>
 struct DecodeCfg {
@@ -51,380 +59,380 @@ struct DecodeCfg {
   static constexpr bool MBF16 = QBF16 || KVF == FMT_BF16;
   static constexpr bool kSplitQ = !QBF16 && MBF16;            // fp16 q, bf16 cache
   static constexpr bool kSplitKV = (KVF == FMT_F16) && MBF16;  // fp16 cache, bf16 q
-  static constexpr int KVB = kFp8 ? 1 : 2;  // bytes per stored element
-  static constexpr int DL = D / 4;          // elements of a row per lane
-  static constexpr int ROWB = DL * KVB;     // bytes of a row per lane
-  static constexpr int U = ROWB / 16;       // 16-byte loads per row per lane
-  static constexpr int NS = D / 32;         // MFMA k-steps for QK
-  static constexpr int NDB = D / 16;        // 16-wide head_dim blocks for PV
-  static constexpr int VROW = D * KVB + 16; // LDS row pitch of the V tile (bytes)
-  static constexpr int VTILE = 32 * VROW;   // LDS bytes per wave
-  static constexpr int MERGE = kDecodeWaves * kDecodeRows * (D + 3) * 4;
-  static constexpr int PIDS = kDecodeWaves * VTILE;            // byte offset of the page-id window
-  static constexpr int LOOP = PIDS + (kPidWindow + 2) * 4;      // LDS used by the main loop
-  static constexpr int LDS = (LOOP > MERGE) ? LOOP : MERGE;
+  static constexpr int KVB = kFp8 ? 1 : 2;    // bytes per stored element
+  static constexpr int DB = D * KVB;          // bytes of one head's row
+  static constexpr int DB16 = DB / 16;        // 16-byte chunks of one head's row
+  static constexpr int DL = D / 4;            // elements of a row a lane multiplies
+  static constexpr int NS = D / 32;           // QK k-steps (MFMA 16x16x32)
+  static constexpr int NDB = D / 16;          // PV head_dim blocks (MFMA 16x16x16)
+  static constexpr int PITCH = kDecodeWaves * DB;   // LDS row pitch: up to 4 heads
+  static constexpr int TILE = kDecodeStep * PITCH;  // one pool, one step
+  static constexpr int STAGE = 2 * TILE;            // K then V
+  static constexpr int PER = kDecodeStep * PITCH / (16 * 256);  // 16-byte loads per thread per pool per step
+  static constexpr int PIDS = 2 * STAGE;            // byte offset of the page-id window
+  static constexpr int PREFIX = PIDS + (kPidWindow + 2) * 4;  // request prefix sums (balanced mode)
+  static constexpr int LDS = PREFIX + (kBalancedMaxBatch + 1) * 8;
 };
 
-template <bool QBF16, int KVF, int D>
-struct KvRegs {
-  using Cfg = DecodeCfg<QBF16, KVF, false, D>;
-  uint4 k[2][Cfg::U];
-  uint4 v[2][Cfg::U];
-};
-
-// Issue the K and V loads of block `blk` for this lane's two tokens
-// (16*h + c, h = 0, 1).  Page ids come from the LDS window `pids` whose first
-// entry is page `pg_lo` of the request; past the chunk end the token index is
-// clamped, and compute() zeroes those rows.
-template <bool QBF16, int KVF, int D>
-__device__ __forceinline__ void issue_kv(const DecodeParams& p, const uint8_t* kb, const uint8_t* vb, int t_begin,
-                                         int t_end, int blk, int c, const int* pids, int pg_lo,
-                                         KvRegs<QBF16, KVF, D>& r) {
-  using Cfg = DecodeCfg<QBF16, KVF, false, D>;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = min(t_begin + 32 * blk + 16 * h + c, t_end - 1);
-    const int pid = pids[(t >> p.page_shift) - pg_lo];
-    const int64_t off = (int64_t)pid * p.sp + (int64_t)(t & (p.page_size - 1)) * p.st;
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + off);
-    const uint4* vp = reinterpret_cast<const uint4*>(vb + off);
-#pragma unroll
-    for (int u = 0; u < Cfg::U; ++u) r.k[h][u] = load16_stream(kp + u);
-#pragma unroll
-    for (int u = 0; u < Cfg::U; ++u) r.v[h][u] = load16_stream(vp + u);
-  }
+// Tokens of request b (0 when it has no pages).
+__device__ __forceinline__ int request_kv_len(const DecodeParams& p, int b) {
+  if (!p.indptr) return p.single_kv_len;
+  const int a = p.indptr[b], e = p.indptr[b + 1];
+  return (e > a) ? (e - a - 1) * p.page_size + p.last_page_len[b] : 0;
 }
-
-// K operand of k-step s for token half h (fp8 widened to the MFMA type; a
-// 2-byte cache as stored).
-template <bool QBF16, int KVF, int D>
-__device__ __forceinline__ uint4 k_operand(const KvRegs<QBF16, KVF, D>& r, int h, int s) {
-  using Cfg = DecodeCfg<QBF16, KVF, false, D>;
-  if constexpr (Cfg::kFp8) {
-    const uint4& x = r.k[h][s >> 1];
-    return (s & 1) ? widen8<Cfg::MBF16, KVF>(x.z, x.w) : widen8<Cfg::MBF16, KVF>(x.x, x.y);
-  } else {
-    return r.k[h][s];
-  }
-}
-
-// Workgroups per CU the register allocation is sized for (4 waves each).
-#ifndef FI_DECODE_MIN_WG_PER_CU
-#define FI_DECODE_MIN_WG_PER_CU 2
-#endif
-// Order of the 1-D grid: chunk index slowest (1) or fastest (0).
-#ifndef FI_DECODE_CHUNK_SLOWEST
-#define FI_DECODE_CHUNK_SLOWEST 0
-#endif
 
 template <bool QBF16, int KVF, bool OBF16, int D>
 __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(const DecodeParams p) {
   using Cfg = DecodeCfg<QBF16, KVF, OBF16, D>;
+  constexpr bool MB = Cfg::MBF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
-  // 1-D grid, chunk index slowest: consecutive workgroups (which the hardware
-  // deals round-robin to the 8 XCDs) walk (kv head slice, request) first, so
-  // the chunk-0 workgroups every request has are spread over all XCDs whatever
-  // the number of chunks.
-  const int units = p.num_kv_heads * p.nsub;
-#if FI_DECODE_CHUNK_SLOWEST
-  const int per_chunk = units * p.batch;
-  const int chunk_id = blockIdx.x / per_chunk;
-  const int rem = blockIdx.x - chunk_id * per_chunk;
-  const int b = rem / units;
-  const int gy = rem - b * units;
-#else
-  const int chunk_id = blockIdx.x % p.max_chunks;
-  const int rem = blockIdx.x / p.max_chunks;
-  const int gy = rem % units;
-  const int b = rem / units;
-#endif
-  const int g = gy / p.nsub;
-  const int sub = gy - g * p.nsub;
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
   const int c = lane & 15;
   const int qg = lane >> 4;
-
-  int kv_len, pg_base;
-  if (p.indptr) {
-    const int a = p.indptr[b], e = p.indptr[b + 1];
-    pg_base = a;
-    kv_len = (e > a) ? (e - a - 1) * p.page_size + p.last_page_len[b] : 0;
-  } else {
-    pg_base = 0;
-    kv_len = p.single_kv_len;
-  }
-  // the host plan sizes the grid from its copy of the page table; clamping keeps
-  // a workgroup inside the partial buffers even if the two copies disagree
-  const int nchunks = min(p.max_chunks, max(1, (kv_len + p.chunk - 1) / p.chunk));
-  if (chunk_id >= nchunks) return;
-  const int t_begin = chunk_id * p.chunk;
-  const int t_end = min(kv_len, t_begin + p.chunk);
-  const int nblk = (t_end > t_begin) ? (t_end - t_begin + 31) / 32 : 0;
-
-  const int rig = sub * kDecodeRows + c;  // row within the GQA group
-  const bool row_ok = rig < p.group;
-  const int h = g * p.group + (row_ok ? rig : 0);
-
-  // Q^T operand: lane (qg, c) holds q[row c][DL*qg + 8s + j], j = 0..7.
-  uint4 qop[Cfg::NS];
-  uint4 qlo[Cfg::kSplitQ ? Cfg::NS : 1];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
-                                                     ((int64_t)b * p.num_qo_heads + h) * D + Cfg::DL * qg);
-#pragma unroll
-    for (int s = 0; s < Cfg::NS; ++s) {
-      const uint4 raw = row_ok ? qp[s] : make_uint4(0, 0, 0, 0);
-      if constexpr (Cfg::kSplitQ) {
-        split_f16x8(raw, qop[s], qlo[s]);
-      } else {
-        qop[s] = raw;
-      }
-    }
-  }
-
-  const uint8_t* kb = p.k + (int64_t)g * p.sh + qg * Cfg::ROWB;
-  const uint8_t* vb = p.v + (int64_t)g * p.sh + qg * Cfg::ROWB;
-  uint8_t* vt = smem + w * Cfg::VTILE;
-  // transposed-read addresses: fp8 tiles give 8 rows per read (lanes 2r, 2r+1
-  // name row r), 2-byte tiles 4 rows per read (lanes 4r..4r+3 name row r)
-  const uint8_t* v_tr;
-  const uint8_t* v_tr2;
-  if constexpr (Cfg::kFp8) {
-    const int rr = c >> 1;
-    const int tok = (rr < 4) ? 4 * qg + rr : 16 + 4 * qg + (rr - 4);
-    v_tr = vt + tok * Cfg::VROW + 8 * (c & 1);
-    v_tr2 = v_tr;
-  } else {
-    v_tr = vt + (4 * qg + (c >> 2)) * Cfg::VROW + 8 * (c & 3);
-    v_tr2 = vt + (16 + 4 * qg + (c >> 2)) * Cfg::VROW + 8 * (c & 3);
-  }
-
-  float m_run = kNegInf;
-  float l_run = 0.f;   // sum of fp32 probabilities (log-sum-exp)
-  float lr_run = 0.f;  // sum of the rounded probabilities (output normalisation)
-  f32x4_t acc[Cfg::NDB];
-#pragma unroll
-  for (int i = 0; i < Cfg::NDB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // One 32-token block: QK on MFMA, online softmax, V through LDS, PV on MFMA.
-  auto compute = [&](int blk, KvRegs<QBF16, KVF, D>& r) {
-    const int tb = t_begin + 32 * blk;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bool ok = tb + 16 * hh + c < t_end;
-#pragma unroll
-      for (int u = 0; u < Cfg::U; ++u) {
-        if (!ok) {
-          r.k[hh][u] = make_uint4(0, 0, 0, 0);
-          r.v[hh][u] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-    // V rows -> LDS (row 16*hh + c, bytes [qg*ROWB, +ROWB)).
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint4* dst = reinterpret_cast<uint4*>(vt + (16 * hh + c) * Cfg::VROW + qg * Cfg::ROWB);
-#pragma unroll
-      for (int u = 0; u < Cfg::U; ++u) dst[u] = r.v[hh][u];
-    }
-    // S^T = K Q^T
-    f32x4_t s[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < Cfg::NS; ++st) {
-        if constexpr (Cfg::kSplitKV) {
-          uint4 khi, klo;
-          split_f16x8(r.k[hh][st], khi, klo);
-          s[hh] = mfma16x16x32<true>(khi, qop[st], s[hh]);
-          s[hh] = mfma16x16x32<true>(klo, qop[st], s[hh]);
-        } else {
-          const uint4 kop = k_operand(r, hh, st);
-          s[hh] = mfma16x16x32<Cfg::MBF16>(kop, qop[st], s[hh]);
-          if constexpr (Cfg::kSplitQ) s[hh] = mfma16x16x32<true>(kop, qlo[st], s[hh]);
-        }
-      }
-    }
-    // online softmax over the block's 32 tokens (row c; 8 values per lane)
-    float x[2][4];
-    float bm = kNegInf;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = tb + 16 * hh + 4 * qg + i < t_end;
-        x[hh][i] = ok ? s[hh][i] * p.scale_log2 : kNegInf;
-        bm = fmaxf(bm, x[hh][i]);
-      }
-    bm = xor_max(bm, 16);
-    bm = xor_max(bm, 32);
-    const float m_new = fmaxf(m_run, bm);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float pe[2][4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pe[hh][i] = fast_exp2(x[hh][i] - m_use);
-    uint4 pop;
-    pop.x = pack2<Cfg::MBF16>(pe[0][0], pe[0][1]);
-    pop.y = pack2<Cfg::MBF16>(pe[0][2], pe[0][3]);
-    pop.z = pack2<Cfg::MBF16>(pe[1][0], pe[1][1]);
-    pop.w = pack2<Cfg::MBF16>(pe[1][2], pe[1][3]);
-    float2 f0 = unpack2<Cfg::MBF16>(pop.x), f1 = unpack2<Cfg::MBF16>(pop.y), f2 = unpack2<Cfg::MBF16>(pop.z),
-           f3 = unpack2<Cfg::MBF16>(pop.w);
-    lr_run = lr_run * alpha + ((f0.x + f0.y) + (f1.x + f1.y)) + ((f2.x + f2.y) + (f3.x + f3.y));
-    l_run = l_run * alpha + ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) +
-            ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < Cfg::NDB; ++i) acc[i] *= alpha;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O^T += V^T P^T: lane (qg, c) needs column 16*db + c of the tile over
-    // tokens 4qg..4qg+3 and 16+4qg..16+4qg+3 (the order its P^T slots hold).
-    // One transposed LDS read per 16-column block gathers exactly that.
-#pragma unroll
-    for (int db = 0; db < Cfg::NDB; ++db) {
-      if constexpr (Cfg::kFp8) {
-        const uint2 x = lds_tr8(v_tr + 16 * db);
-        acc[db] = mfma16x16x32<Cfg::MBF16>(widen8<Cfg::MBF16, KVF>(x.x, x.y), pop, acc[db]);
-      } else {
-        const uint2 x1 = lds_tr16(v_tr + 32 * db);
-        const uint2 x2 = lds_tr16(v_tr2 + 32 * db);
-        const uint4 vraw = make_uint4(x1.x, x1.y, x2.x, x2.y);
-        if constexpr (Cfg::kSplitKV) {
-          uint4 vhi, vlo;
-          split_f16x8(vraw, vhi, vlo);
-          acc[db] = mfma16x16x32<true>(vhi, pop, acc[db]);
-          acc[db] = mfma16x16x32<true>(vlo, pop, acc[db]);
-        } else {
-          acc[db] = mfma16x16x32<Cfg::MBF16>(vraw, pop, acc[db]);
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  // The chunk's page ids are staged in LDS, a window of kPidWindow pages at a
-  // time, so that no K/V load waits on a page-id load.  Each wave then runs a
-  // two-deep software pipeline over its blocks (w, w+4, ...): the loads of the
-  // next block are in flight while a block is computed, and the wait before a
-  // block covers only that block's loads.  Past the wave's last block the
-  // index is clamped to it, so the extra loads re-read cached lines.
+  const int groups = p.n_hgroups * p.n_sgroups;
   int* pids_s = reinterpret_cast<int*>(smem + Cfg::PIDS);
   const int shift = p.page_shift;
-  const int win_blocks =
-      (int)min((int64_t)max(nblk, 1), max((int64_t)kDecodeWaves, ((int64_t)kPidWindow << shift) / 32));
-  for (int wb0 = 0; wb0 < nblk; wb0 += win_blocks) {
-    const int wb1 = min(nblk, wb0 + win_blocks);
-    const int pg_lo = (t_begin + 32 * wb0) >> shift;
-    const int pg_hi = ((min(t_begin + 32 * wb1, t_end) - 1) >> shift) + 1;
-    const int cnt = min(pg_hi - pg_lo, kPidWindow + 2);
-    __syncthreads();  // the previous window's page ids are no longer read
-    for (int i = threadIdx.x; i < cnt; i += 256) pids_s[i] = p.indices ? p.indices[pg_base + pg_lo + i] : 0;
-    __syncthreads();
-    const int my_n = (wb1 - wb0 > w) ? (wb1 - wb0 - w + kDecodeWaves - 1) / kDecodeWaves : 0;
-    if (my_n > 0) {
-      auto blk_of = [&](int k) { return wb0 + w + kDecodeWaves * min(k, my_n - 1); };
-      KvRegs<QBF16, KVF, D> ra, rb;
-      issue_kv(p, kb, vb, t_begin, t_end, blk_of(0), c, pids_s, pg_lo, ra);
-      for (int k = 0; k < my_n; k += 2) {
-        issue_kv(p, kb, vb, t_begin, t_end, blk_of(k + 1), c, pids_s, pg_lo, rb);
-        compute(blk_of(k), ra);
-        if (k + 1 >= my_n) break;
-        issue_kv(p, kb, vb, t_begin, t_end, blk_of(k + 2), c, pids_s, pg_lo, ra);
-        compute(blk_of(k + 1), rb);
+  const int hpw = 1 << p.hpw_shift;
+  const int cpr_shift = __builtin_ctz(Cfg::DB16) + p.hpw_shift;
+  const int cpr = 1 << cpr_shift;    // 16-byte chunks per token row of the workgroup's heads
+  const int swz = min(cpr - 1, 7);   // XOR swizzle of a row's 16-byte chunks
+
+  // Work on one piece: tokens [t_begin, t_end) of request b, head/slice group
+  // grp, which is chunk `chunk_id` of the `nchunks` pieces of its segment.
+  auto process = [&](int b, int grp, int t_begin, int t_end, int chunk_id, int nchunks) {
+    const int hgrp = grp % p.n_hgroups;
+    const int sgrp = grp / p.n_hgroups;
+    const int pg_base = p.indptr ? p.indptr[b] : 0;
+    const int nsteps = (t_end > t_begin) ? (t_end - t_begin + kDecodeStep - 1) / kDecodeStep : 0;
+
+    // this wave's (kv head, slice) and the workgroup's heads
+    const int g0 = hgrp << p.hpw_shift;
+    const int hl = w / p.spw;                         // head within the workgroup
+    const int sub = sgrp * p.spw + (w - hl * p.spw);  // 16-row slice of the GQA group
+    const bool wave_ok = hl < hpw && sub < p.nsub;
+    const int g = g0 + (wave_ok ? hl : 0);
+    const int rig = sub * kDecodeRows + c;            // row within the GQA group
+    const bool row_ok = wave_ok && rig < p.group;
+    const int h = g * p.group + (row_ok ? rig : 0);
+
+    // Q^T operand: lane (qg, c) holds q[row c][DL*qg + 8s + j], j = 0..7.
+    uint4 qop[Cfg::NS];
+    uint4 qlo[Cfg::kSplitQ ? Cfg::NS : 1];
+    {
+      const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                                       ((int64_t)b * p.num_qo_heads + h) * D + Cfg::DL * qg);
+#pragma unroll
+      for (int s = 0; s < Cfg::NS; ++s) {
+        const uint4 raw = row_ok ? qp[s] : make_uint4(0, 0, 0, 0);
+        if constexpr (Cfg::kSplitQ) {
+          split_f16x8(raw, qop[s], qlo[s]);
+        } else {
+          qop[s] = raw;
+        }
       }
     }
-  }
 
-  // Per-wave state -> LDS, then merge the four waves.
-  l_run = xor_sum(l_run, 16);
-  l_run = xor_sum(l_run, 32);
-  lr_run = xor_sum(lr_run, 16);
-  lr_run = xor_sum(lr_run, 32);
-  __syncthreads();
-  float* ms = reinterpret_cast<float*>(smem);                 // [4][16]
-  float* ls = ms + kDecodeWaves * kDecodeRows;                 // [4][16]
-  float* lrs = ls + kDecodeWaves * kDecodeRows;                // [4][16]
-  float* accs = lrs + kDecodeWaves * kDecodeRows;              // [4][16][D]
-  if (qg == 0) {
-    ms[w * kDecodeRows + c] = m_run;
-    ls[w * kDecodeRows + c] = l_run;
-    lrs[w * kDecodeRows + c] = lr_run;
-  }
+    // Cooperative loads: thread tid moves 16-byte chunks ci = j*256 + tid
+    // (j < PER) of each pool; chunk ci is row ci / cpr, 16-byte column
+    // ci % cpr of the workgroup's contiguous heads.  With fewer than 4 heads
+    // the surplus threads repeat a chunk another thread moves (same address,
+    // same value).
+    int ld_row[Cfg::PER], ld_col[Cfg::PER];
+    int64_t ld_off[Cfg::PER];
 #pragma unroll
-  for (int db = 0; db < Cfg::NDB; ++db) {
-    *reinterpret_cast<f32x4_t*>(accs + (w * kDecodeRows + c) * D + 16 * db + 4 * qg) = acc[db];
-  }
-  __syncthreads();
-
-  constexpr int EPT = D * kDecodeRows / 256;  // outputs per thread (8 or 4)
-  const int row = threadIdx.x / 16;
-  const int d0 = (threadIdx.x % 16) * EPT;
-  const int rrow = sub * kDecodeRows + row;
-  if (rrow >= p.group) return;
-  const int hq = g * p.group + rrow;
-  float M = kNegInf;
-#pragma unroll
-  for (int ww = 0; ww < kDecodeWaves; ++ww) M = fmaxf(M, ms[ww * kDecodeRows + row]);
-  float wt[kDecodeWaves];
-  float L = 0.f, Lr = 0.f;
-#pragma unroll
-  for (int ww = 0; ww < kDecodeWaves; ++ww) {
-    const float mw = ms[ww * kDecodeRows + row];
-    wt[ww] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-    L += wt[ww] * ls[ww * kDecodeRows + row];
-    Lr += wt[ww] * lrs[ww * kDecodeRows + row];
-  }
-  float out[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    float a = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kDecodeWaves; ++ww) a += wt[ww] * accs[(ww * kDecodeRows + row) * D + d0 + e];
-    out[e] = a;
-  }
-  const float inv = (Lr > 0.f) ? 1.f / Lr : 0.f;
-  const float lse2 = (L > 0.f) ? M + fast_log2(L) : kNegInf;
-  if (nchunks == 1) {
-    const float f = inv * p.v_scale;
-    uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + d0;
-    uint32_t packed[EPT / 2];
-#pragma unroll
-    for (int e = 0; e < EPT / 2; ++e) packed[e] = pack2<OBF16>(out[2 * e] * f, out[2 * e + 1] * f);
-    if constexpr (EPT == 8) {
-      *reinterpret_cast<uint4*>(op) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    } else {
-      *reinterpret_cast<uint2*>(op) = make_uint2(packed[0], packed[1]);
+    for (int j = 0; j < Cfg::PER; ++j) {
+      const int ci = (j * 256 + tid) & (kDecodeStep * cpr - 1);
+      ld_row[j] = ci >> cpr_shift;
+      ld_col[j] = ci & (cpr - 1);
+      const int hh = ld_col[j] / Cfg::DB16;
+      ld_off[j] = (int64_t)(g0 + hh) * p.sh + (ld_col[j] - hh * Cfg::DB16) * 16;
     }
-    if (p.lse && (threadIdx.x % 16) == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = lse2 * kLn2;
-  } else {
-    const int64_t pidx = ((int64_t)b * p.max_chunks + chunk_id) * p.num_qo_heads + hq;
-    float* po = p.part_o + pidx * D + d0;
+    int pg_lo = 0;
+    struct Regs {
+      uint4 k[Cfg::PER];
+      uint4 v[Cfg::PER];
+    };
+    auto load_step = [&](int st, Regs& r) {
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4)
-      *reinterpret_cast<f32x4_t*>(po + e) = f32x4_t{out[e] * inv, out[e + 1] * inv, out[e + 2] * inv, out[e + 3] * inv};
-    if ((threadIdx.x % 16) == 0) p.part_lse[pidx] = lse2;
+      for (int j = 0; j < Cfg::PER; ++j) {
+        const int t = min(t_begin + st * kDecodeStep + ld_row[j], t_end - 1);
+        const int pid = pids_s[(t >> shift) - pg_lo];
+        const int64_t off = (int64_t)pid * p.sp + (int64_t)(t & (p.page_size - 1)) * p.st + ld_off[j];
+        r.k[j] = load16_stream(p.k + off);
+        r.v[j] = load16_stream(p.v + off);
+      }
+    };
+    auto store_step = [&](int st, Regs& r, uint8_t* stage) {
+#pragma unroll
+      for (int j = 0; j < Cfg::PER; ++j) {
+        const bool ok = t_begin + st * kDecodeStep + ld_row[j] < t_end;
+        const int o = ld_row[j] * Cfg::PITCH + 16 * (ld_col[j] ^ (ld_row[j] & swz));
+        *reinterpret_cast<uint4*>(stage + o) = ok ? r.k[j] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(stage + Cfg::TILE + o) = ok ? r.v[j] : make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    float m_run = kNegInf;
+    float l_run = 0.f;   // sum of fp32 probabilities (log-sum-exp)
+    float lr_run = 0.f;  // sum of the rounded probabilities (output normalisation)
+    f32x4_t acc[Cfg::NDB];
+#pragma unroll
+    for (int i = 0; i < Cfg::NDB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // K: lane (qg, c) reads token c, bytes [hl*DB + qg*DL*KVB, +DL*KVB) of its head
+    const int kcol0 = hl * Cfg::DB16 + qg * (Cfg::DL * Cfg::KVB / 16);
+    const int k_off = c * Cfg::PITCH;
+    // V: transposed reads, see the PV step
+    int v_off[Cfg::kFp8 ? Cfg::NDB / 2 : Cfg::NDB];
+    if constexpr (Cfg::kFp8) {
+      // lanes 2r, 2r+1 name row r: token 4qg + (r & 3), head_dim block 2i + (r >> 2)
+      const int r = c >> 1;
+      const int tok = 4 * qg + (r & 3);
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB / 2; ++i) {
+        const int col = hl * Cfg::DB16 + 2 * i + (r >> 2);
+        v_off[i] = Cfg::TILE + tok * Cfg::PITCH + 16 * (col ^ (tok & swz)) + 8 * (c & 1);
+      }
+    } else {
+      // lanes 4r..4r+3 name row r: token 4qg + r, the four 8-byte pieces of a
+      // 16-wide head_dim block (32 bytes)
+      const int r = c >> 2, q4 = c & 3;
+      const int tok = 4 * qg + r;
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB; ++i) {
+        const int col = hl * Cfg::DB16 + 2 * i + (q4 >> 1);
+        v_off[i] = Cfg::TILE + tok * Cfg::PITCH + 16 * (col ^ (tok & swz)) + 8 * (q4 & 1);
+      }
+    }
+
+    auto compute = [&](int st, const uint8_t* stage) {
+      const int tb = t_begin + st * kDecodeStep;
+      // S^T = K Q^T over the step's 16 tokens
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < Cfg::DL * Cfg::KVB / 16; ++u) {
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + k_off + 16 * ((kcol0 + u) ^ (c & swz)));
+        if constexpr (Cfg::kFp8) {
+          s = mfma16x16x32<MB>(widen8<MB, KVF>(x.x, x.y), qop[2 * u], s);
+          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(widen8<MB, KVF>(x.x, x.y), qlo[2 * u], s);
+          s = mfma16x16x32<MB>(widen8<MB, KVF>(x.z, x.w), qop[2 * u + 1], s);
+          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(widen8<MB, KVF>(x.z, x.w), qlo[2 * u + 1], s);
+        } else if constexpr (Cfg::kSplitKV) {
+          uint4 khi, klo;
+          split_f16x8(x, khi, klo);
+          s = mfma16x16x32<true>(khi, qop[u], s);
+          s = mfma16x16x32<true>(klo, qop[u], s);
+        } else {
+          s = mfma16x16x32<MB>(x, qop[u], s);
+          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(x, qlo[u], s);
+        }
+      }
+      // online softmax: lane (qg, c) holds tokens tb + 4qg + i of row c
+      float x[4];
+      float bm = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (tb + 4 * qg + i < t_end) ? s[i] * p.scale_log2 : kNegInf;
+        bm = fmaxf(bm, x[i]);
+      }
+      bm = xor_max(bm, 16);
+      bm = xor_max(bm, 32);
+      const float m_new = fmaxf(m_run, bm);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float pe[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - m_use);
+      const uint2 pop = make_uint2(pack2<MB>(pe[0], pe[1]), pack2<MB>(pe[2], pe[3]));
+      const float2 f0 = unpack2<MB>(pop.x), f1 = unpack2<MB>(pop.y);
+      lr_run = lr_run * alpha + ((f0.x + f0.y) + (f1.x + f1.y));
+      l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB; ++i) acc[i] *= alpha;
+      // O^T += V^T P^T (MFMA 16x16x16): lane (qg, c) needs column 16*db + c of
+      // tokens 4qg..4qg+3, the order its P^T slots hold.
+      if constexpr (Cfg::kFp8) {
+#pragma unroll
+        for (int i = 0; i < Cfg::NDB / 2; ++i) {
+          const uint2 v = lds_tr8(stage + v_off[i]);
+          acc[2 * i] = mfma16x16x16<MB>(widen4<MB, KVF>(v.x), pop, acc[2 * i]);
+          acc[2 * i + 1] = mfma16x16x16<MB>(widen4<MB, KVF>(v.y), pop, acc[2 * i + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::NDB; ++i) {
+          const uint2 v = lds_tr16(stage + v_off[i]);
+          if constexpr (Cfg::kSplitKV) {
+            uint2 vhi, vlo;
+            split_f16x2(v.x, vhi.x, vlo.x);
+            split_f16x2(v.y, vhi.y, vlo.y);
+            acc[i] = mfma16x16x16<true>(vhi, pop, acc[i]);
+            acc[i] = mfma16x16x16<true>(vlo, pop, acc[i]);
+          } else {
+            acc[i] = mfma16x16x16<MB>(v, pop, acc[i]);
+          }
+        }
+      }
+    };
+
+    // Page ids are staged in LDS a window of kPidWindow pages at a time, so
+    // that no K/V load waits on a page-id load.  Within a window the loads of
+    // the next two steps are in flight while a step is computed; every step
+    // costs one barrier (it publishes the stage just written, and tells the
+    // writer of the other stage that its previous readers are done).  Past
+    // the last step the step index is clamped, so the extra loads re-read
+    // cached lines.
+    const int win_steps =
+        (int)min((int64_t)max(nsteps, 1), max((int64_t)1, ((int64_t)kPidWindow << shift) / kDecodeStep));
+    for (int ws0 = 0; ws0 < nsteps; ws0 += win_steps) {
+      const int ws1 = min(nsteps, ws0 + win_steps);
+      pg_lo = (t_begin + ws0 * kDecodeStep) >> shift;
+      const int pg_hi = ((min(t_begin + ws1 * kDecodeStep, t_end) - 1) >> shift) + 1;
+      const int cnt = min(pg_hi - pg_lo, kPidWindow + 2);
+      __syncthreads();  // the previous stages and page ids are no longer read
+      for (int i = tid; i < cnt; i += 256) pids_s[i] = p.indices ? p.indices[pg_base + pg_lo + i] : 0;
+      __syncthreads();
+      const int n = ws1 - ws0;
+      auto step_of = [&](int k) { return ws0 + min(k, n - 1); };
+      Regs ra, rb;
+      load_step(step_of(0), ra);
+      load_step(step_of(1), rb);
+      for (int k = 0; k < n; k += 2) {
+        store_step(step_of(k), ra, smem);
+        load_step(step_of(k + 2), ra);
+        __syncthreads();
+        if (wave_ok) compute(step_of(k), smem);
+        if (k + 1 >= n) break;
+        store_step(step_of(k + 1), rb, smem + Cfg::STAGE);
+        load_step(step_of(k + 3), rb);
+        __syncthreads();
+        if (wave_ok) compute(step_of(k + 1), smem + Cfg::STAGE);
+      }
+    }
+
+    // every wave writes its own rows
+    if (chunk_id == 0 && tid == 0 && p.nch) p.nch[(int64_t)b * groups + grp] = nchunks;
+    l_run = xor_sum(l_run, 16);
+    l_run = xor_sum(l_run, 32);
+    lr_run = xor_sum(lr_run, 16);
+    lr_run = xor_sum(lr_run, 32);
+    if (!row_ok) return;
+    const float inv = (lr_run > 0.f) ? 1.f / lr_run : 0.f;
+    const float lse2 = (l_run > 0.f) ? m_run + fast_log2(l_run) : kNegInf;
+    if (nchunks == 1) {
+      const float f = inv * p.v_scale;
+      uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + h) * D + 4 * qg;
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB; ++i)
+        *reinterpret_cast<uint2*>(op + 16 * i) =
+            make_uint2(pack2<OBF16>(acc[i][0] * f, acc[i][1] * f), pack2<OBF16>(acc[i][2] * f, acc[i][3] * f));
+      if (p.lse && qg == 0) p.lse[(int64_t)b * p.num_qo_heads + h] = lse2 * kLn2;
+    } else if (p.part_o && chunk_id < p.max_chunks) {
+      const int64_t pidx = ((int64_t)b * p.num_qo_heads + h) * p.max_chunks + chunk_id;
+      float* po = p.part_o + pidx * D + 4 * qg;
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB; ++i) *reinterpret_cast<f32x4_t*>(po + 16 * i) = acc[i] * inv;
+      if (qg == 0) p.part_lse[pidx] = lse2;
+    }
+  };
+
+  if (!p.balanced) {
+    // Fixed chunks: 1-D grid, chunk index fastest, then group, then request.
+    const int chunk_id = blockIdx.x % p.max_chunks;
+    const int rem = blockIdx.x / p.max_chunks;
+    const int grp = rem % groups;
+    const int b = rem / groups;
+    const int kv_len = request_kv_len(p, b);
+    // the host sizes the grid from its copy of the page table; clamping keeps a
+    // workgroup inside the partial buffers even if the two copies disagree
+    const int nchunks = min(p.max_chunks, max(1, (kv_len + p.chunk - 1) / p.chunk));
+    if (chunk_id >= nchunks) return;
+    const int t_begin = chunk_id * p.chunk;
+    process(b, grp, t_begin, min(kv_len, t_begin + p.chunk), chunk_id, nchunks);
+    return;
+  }
+
+  // Balanced slices: the (group, request, token) space of groups x T items
+  // (T = total tokens) is cut into equal slices of p.slice items, one per
+  // workgroup, so every workgroup streams the same number of bytes.  A slice
+  // may cover the end of one request and the start of the next; each such
+  // piece is a chunk of its (request, group) segment.
+  int64_t* pre = reinterpret_cast<int64_t*>(smem + Cfg::PREFIX);  // [batch + 1] token prefix sums
+  {
+    const int B = p.batch;
+    const int per = (B + 255) / 256;
+    int64_t local = 0;
+    for (int k = 0; k < per; ++k) {
+      const int i = tid * per + k;
+      if (i < B) local += request_kv_len(p, i);
+    }
+    int64_t v = local;  // inclusive scan over the workgroup
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t n = __shfl_up(v, o);
+      if (lane >= o) v += n;
+    }
+    __shared__ int64_t wsum[4];
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    for (int ww = 0; ww < w; ++ww) v += wsum[ww];
+    int64_t run = v - local;  // exclusive prefix of this thread's first element
+    for (int k = 0; k < per; ++k) {
+      const int i = tid * per + k;
+      if (i < B) {
+        pre[i] = run;
+        run += request_kv_len(p, i);
+      }
+    }
+    if (tid == 0) pre[B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  const int64_t T = pre[p.batch];
+  const int64_t W = T * groups;
+  int64_t x0 = (int64_t)blockIdx.x * p.slice;
+  const int64_t x1 = min(W, x0 + p.slice);
+  while (x0 < x1) {
+    const int grp = (int)(x0 / T);
+    const int64_t pos = x0 - grp * T;
+    int lo = 0, hi = p.batch;  // largest b with pre[b] <= pos (then pos < pre[b + 1])
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= pos) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int64_t seg0 = grp * T + pre[b];
+    const int64_t seg1 = grp * T + pre[b + 1];
+    const int64_t end = min(seg1, x1);
+    const int64_t w_first = seg0 / p.slice;
+    const int nchunks = (int)((seg1 - 1) / p.slice - w_first + 1);
+    process(b, grp, (int)(pos - pre[b]), (int)(end - seg0), (int)(blockIdx.x - w_first), nchunks);
+    x0 = end;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Split-KV merge: L = log2 sum_c 2^lse_c, o = v_scale * sum_c 2^(lse_c - L) o_c
 // (the natural-log form of the same identity is the oracle's merge_states).
-// One wave per (request, q head); lanes cover head_dim.
+// One workgroup per (request, q head).  A (request, head) pair's partials are
+// contiguous over chunks, so the 256 threads stream them: thread t owns the
+// 4-float column quad t % (D/4) of every (256 / (D/4))-th chunk, and the
+// per-thread sums are reduced through LDS.
 // ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
 template <bool OBF16, int D>
-__global__ __launch_bounds__(64) void merge_kernel(const MergeParams p) {
-  const int hq = blockIdx.x;
-  const int b = blockIdx.y;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeParams p) {
+  constexpr int QUADS = D / 4;                      // float4 columns of a row
+  constexpr int LANES = kMergeThreads / QUADS;      // chunks processed side by side
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4_t part[LANES][QUADS];
+  const int hq = blockIdx.x % p.num_qo_heads;
+  const int b = blockIdx.x / p.num_qo_heads;
+  const int tid = threadIdx.x;
   int kv_len;
   if (p.indptr) {
     const int a = p.indptr[b], e = p.indptr[b + 1];
@@ -432,34 +440,60 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeParams p) {
   } else {
     kv_len = p.single_kv_len;
   }
-  const int nchunks = min(p.max_chunks, max(1, (kv_len + p.chunk - 1) / p.chunk));
+  if (kv_len == 0) {  // a request without keys: o = 0, lse = -inf
+    if (tid < QUADS) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + 4 * tid;
+      *reinterpret_cast<uint2*>(op) = make_uint2(0u, 0u);
+    }
+    if (p.lse && tid == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = kNegInf;
+    return;
+  }
+  // the (head group, slice group) this q head belongs to, as the decode kernel numbers them
+  const int gkv = hq / p.group;
+  const int sub = (hq - gkv * p.group) / kDecodeRows;
+  const int grp = (sub / p.spw) * p.n_hgroups + (gkv >> p.hpw_shift);
+  const int nchunks = min(p.max_chunks, p.nch[(int64_t)b * p.n_hgroups * p.n_sgroups + grp]);
   if (nchunks <= 1) return;
-  constexpr int EPL = D / 64;
-  const int lane = threadIdx.x;
-  const int64_t base = (int64_t)b * p.max_chunks * p.num_qo_heads + hq;
+  const int64_t base = ((int64_t)b * p.num_qo_heads + hq) * p.max_chunks;
+  const float* lse = p.part_lse + base;
+  // block max of the chunks' log-sum-exps
   float M = kNegInf;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, p.part_lse[base + (int64_t)c * p.num_qo_heads]);
-  float L = 0.f;
-  float acc[EPL];
+  for (int c = tid; c < nchunks; c += kMergeThreads) M = fmaxf(M, lse[c]);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t idx = base + (int64_t)c * p.num_qo_heads;
-    const float lc = p.part_lse[idx];
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  // weighted sums
+  const int q = tid % QUADS;
+  const int ln = tid / QUADS;
+  float L = 0.f;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const f32x4_t* po = reinterpret_cast<const f32x4_t*>(p.part_o + base * D) + q;
+#pragma unroll 4
+  for (int c = ln; c < nchunks; c += LANES) {
+    const float lc = lse[c];
     const float wgt = (lc == kNegInf) ? 0.f : fast_exp2(lc - M);
     L += wgt;
-    const float* po = p.part_o + idx * D + lane * EPL;
+    acc += wgt * po[(int64_t)c * QUADS];
+  }
+  part[ln][q] = acc;
+  // L: every thread of a column quad saw a disjoint set of chunks; sum over them
+  float Ls = (q == 0) ? L : 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += wgt * po[e];
-  }
-  const float f = (L > 0.f) ? p.v_scale / L : 0.f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + lane * EPL;
-  if constexpr (EPL == 2) {
-    *reinterpret_cast<uint32_t*>(op) = pack2<OBF16>(acc[0] * f, acc[1] * f);
-  } else {
-    op[0] = to_bits<OBF16>(acc[0] * f);
-  }
-  if (p.lse && lane == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o);
+  if ((tid & 63) == 0) red[tid >> 6] = Ls;
+  __syncthreads();
+  if (tid >= QUADS) return;
+  const float Lt = red[0] + red[1] + red[2] + red[3];
+  f32x4_t sum = part[0][q];
+#pragma unroll
+  for (int l = 1; l < LANES; ++l) sum += part[l][q];
+  const float f = (Lt > 0.f) ? p.v_scale / Lt : 0.f;
+  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + 4 * q;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack2<OBF16>(sum[0] * f, sum[1] * f), pack2<OBF16>(sum[2] * f, sum[3] * f));
+  if (p.lse && tid == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = (Lt > 0.f) ? (M + fast_log2(Lt)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +520,8 @@ __global__ __launch_bounds__(256) void widen_kernel(const uint8_t* codes, int64_
 // ---------------------------------------------------------------------------
 template <bool QBF16, int KVF, bool OBF16, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int batch, hipStream_t s) {
-  dim3 grid((unsigned)p.max_chunks * p.num_kv_heads * p.nsub * batch);
+  dim3 grid(p.balanced ? (unsigned)p.n_wg : (unsigned)p.max_chunks * p.n_hgroups * p.n_sgroups * batch);
+  if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL((decode_kernel<QBF16, KVF, OBF16, D>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -514,6 +549,48 @@ static hipError_t launch_decode_kv(const DecodeParams& p, int kv_fmt, int o_fmt,
   }
 }
 
+template <bool QBF16, int KVF, bool OBF16, int D>
+static int occupancy_t() {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&decode_kernel<QBF16, KVF, OBF16, D>),
+                                                   256, 0) != hipSuccess)
+    return 0;
+  return occ;
+}
+
+template <bool QBF16, int KVF, bool OBF16>
+static int occupancy_d(int d) { return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128>() : occupancy_t<QBF16, KVF, OBF16, 64>(); }
+
+template <bool QBF16, int KVF>
+static int occupancy_o(int o, int d) { return o == FMT_BF16 ? occupancy_d<QBF16, KVF, true>(d) : occupancy_d<QBF16, KVF, false>(d); }
+
+template <bool QBF16>
+static int occupancy_kv(int kv, int o, int d) {
+  switch (kv) {
+    case FMT_F16: return occupancy_o<QBF16, FMT_F16>(o, d);
+    case FMT_BF16: return occupancy_o<QBF16, FMT_BF16>(o, d);
+    case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3>(o, d);
+    default: return occupancy_o<QBF16, FMT_E5M2>(o, d);
+  }
+}
+
+int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
+  // cached per (device, instantiation): the values cannot change while the process runs
+  static std::atomic<int> cache[64][2][5][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::atomic<int>& slot = cache[dev][q_fmt == FMT_BF16][kv_fmt][o_fmt == FMT_BF16][head_dim == 128];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int occ = q_fmt == FMT_BF16 ? occupancy_kv<true>(kv_fmt, o_fmt, head_dim)
+                                     : occupancy_kv<false>(kv_fmt, o_fmt, head_dim);
+  v = cus * occ;
+  slot.store(v, std::memory_order_relaxed);
+  return v;
+}
+
 hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                          hipStream_t s) {
   if (q_fmt == FMT_BF16) return launch_decode_kv<true>(p, kv_fmt, o_fmt, head_dim, batch, s);
@@ -521,17 +598,18 @@ hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt
 }
 
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {
-  dim3 grid(p.num_qo_heads, batch);
+  dim3 grid((unsigned)p.num_qo_heads * batch);
+  dim3 block(kMergeThreads);
   if (o_fmt == FMT_BF16) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((merge_kernel<true, 128>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((merge_kernel<true, 128>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((merge_kernel<true, 64>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((merge_kernel<true, 64>), grid, block, 0, s, p);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((merge_kernel<false, 128>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((merge_kernel<false, 128>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((merge_kernel<false, 64>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((merge_kernel<false, 64>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

@@ -10,11 +10,12 @@ namespace fi {
 // Stored element formats; the values match fi_dtype.
 enum Fmt : int { FMT_F16 = 1, FMT_BF16 = 2, FMT_E4M3 = 3, FMT_E5M2 = 4 };
 
-constexpr int kDecodeWaves = 4;         // waves per decode workgroup
-constexpr int kDecodeBlock = 32;        // tokens per wave step
-constexpr int kChunkQuantum = kDecodeWaves * kDecodeBlock;  // split-KV chunk granularity
-constexpr int kDecodeRows = 16;         // q rows per decode MFMA tile (one GQA subgroup)
+constexpr int kDecodeWaves = 4;         // waves per decode workgroup, one (kv head, row slice) each
+constexpr int kDecodeStep = 16;         // tokens staged per step
+constexpr int kChunkQuantum = 64;       // split-KV chunk granularity (tokens)
+constexpr int kDecodeRows = 16;         // q rows per decode MFMA tile (one GQA slice)
 constexpr float kLog2eHost = 1.4426950408889634f;
+constexpr int kBalancedMaxBatch = 1024; // largest batch the balanced decode split handles
 
 struct DecodeParams {
   const void* q;          // [tokens, Hqo, D]
@@ -32,14 +33,22 @@ struct DecodeParams {
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;          // Hqo / Hkv
-  int32_t nsub;           // ceil(group / 16)
-  int32_t chunk;          // tokens per workgroup (multiple of kChunkQuantum)
-  int32_t max_chunks;     // chunks of the longest request
+  int32_t nsub;           // 16-row slices of a GQA group: ceil(group / 16)
+  int32_t hpw_shift;      // log2(kv heads per workgroup): 0, 1 or 2
+  int32_t spw;            // slices per workgroup (waves = heads x slices <= 4)
+  int32_t n_hgroups;      // kv head groups: num_kv_heads >> hpw_shift
+  int32_t n_sgroups;      // slice groups: ceil(nsub / spw)
+  int32_t chunk;          // fixed chunks: tokens per workgroup (multiple of kChunkQuantum)
+  int32_t max_chunks;     // pieces a (request, group) segment can have: partial buffer stride
   int32_t batch;
+  int32_t balanced;       // 1: equal slices of the (group, request, token) space
+  int32_t n_wg;           // balanced: workgroups launched
+  int64_t slice;          // balanced: (group x token) items per workgroup
+  int32_t* nch;           // [batch, groups] pieces per segment, written for the merge (or null)
   float scale_log2;       // sm_scale * k_scale * log2(e)
   float v_scale;
-  float* part_o;          // [batch, max_chunks, Hqo, D] fp32, normalised, unscaled by v_scale
-  float* part_lse;        // [batch, max_chunks, Hqo] base-2 log-sum-exp
+  float* part_o;          // [batch, Hqo, max_chunks, D] fp32, normalised, unscaled by v_scale
+  float* part_lse;        // [batch, Hqo, max_chunks] base-2 log-sum-exp
 };
 
 struct MergeParams {
@@ -47,12 +56,14 @@ struct MergeParams {
   float* lse;
   const float* part_o;
   const float* part_lse;
+  const int32_t* nch;     // [batch, groups] pieces per segment
   const int32_t* indptr;
   const int32_t* last_page_len;
   int32_t page_size;
   int32_t single_kv_len;
   int32_t num_qo_heads;
-  int32_t chunk;
+  int32_t group;          // q heads per kv head
+  int32_t hpw_shift, spw, n_hgroups, n_sgroups;
   int32_t max_chunks;
   float v_scale;
 };
@@ -86,6 +97,8 @@ struct PrefillParams {
 hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                          hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s);
+// Workgroups of the decode kernel for these types that fit on the current device at once.
+int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim);
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                           hipStream_t s);
 hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int dst_fmt, void* out, hipStream_t s);

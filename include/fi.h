@@ -134,7 +134,9 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
  *   q        [dev] [batch, num_qo_heads, head_dim], q_dtype in {FI_F16, FI_BF16}
  *   kv       the paged cache; KV dtype in {F16, BF16, E4M3, E5M2}.  A 2-byte KV
  *            dtype may differ from q's ([C] design notes: mixed 2-byte decode
- *            is correct); its values are converted to q's type on load.
+ *            is correct); the products then run in bf16 with every fp16
+ *            value split exactly into two bf16 parts, so nothing is rounded
+ *            and nothing can overflow.
  *   o        [dev] [batch, num_qo_heads, head_dim] of o_dtype
  *            (FI_DTYPE_DEFAULT = q_dtype; fp8 refused)
  *   lse      [dev] [batch, num_qo_heads] float32, or NULL
@@ -143,7 +145,7 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
  *            least fi_decode_workspace_bytes(batch, num_qo_heads, head_dim,
  *            longest kv_len).
  * Environment: FI_SPLIT_KV = "off" disables splitting, a positive integer
- * forces that many tokens per chunk (rounded up to a multiple of 128), unset
+ * forces that many tokens per chunk (rounded up to a multiple of 64), unset
  * or "auto" lets the planner choose (fixed_split_size). */
 fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
                                 const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,

@@ -56,10 +56,10 @@ def test_exports_every_declared_symbol(L):
 
 def test_workspace_bound(L):
     assert fi.fi_decode_workspace_bytes(0, 32, 128, 4096) == 0
-    # B * ceil(max_kv / 128) chunks * H_qo * (D + 1) floats
-    assert fi.fi_decode_workspace_bytes(64, 32, 128, 4096) == 64 * 32 * 32 * 129 * 4
-    assert fi.fi_decode_workspace_bytes(8, 64, 128, 131072) == 8 * 1024 * 64 * 129 * 4
-    assert fi.fi_decode_workspace_bytes(1, 4, 64, 1) == 1 * 2 * 4 * 65 * 4
+    # B * H_qo * (ceil(max_kv / 64) + 1) pieces * (D + 1) floats, plus B * H_qo piece counts
+    assert fi.fi_decode_workspace_bytes(64, 32, 128, 4096) == 64 * 32 * 65 * 129 * 4 + 64 * 32 * 4
+    assert fi.fi_decode_workspace_bytes(8, 64, 128, 131072) == 8 * 64 * 2049 * 129 * 4 + 8 * 64 * 4
+    assert fi.fi_decode_workspace_bytes(1, 4, 64, 1) == 1 * 4 * 2 * 65 * 4 + 4 * 4
 
 
 def _kv(k_dtype="e4m3", v_dtype=None, *, page=16, hkv=2, d=64, lens=(5, 17), ptrs=False, lpl=None):
