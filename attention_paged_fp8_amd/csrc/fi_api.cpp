@@ -121,6 +121,8 @@ fi_status check_paged(const char* fn, int32_t batch, const fi_paged_kv* kv, int6
   if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0)
     return fail(FI_E_SHAPE, fn, "strides must be positive (page %lld, token %lld, head %lld)",
                 (long long)kv->stride_page, (long long)kv->stride_token, (long long)kv->stride_head);
+  if (kv->stride_page * eb >= (1ll << 32) || kv->stride_token * eb >= (1ll << 32) || kv->stride_head * eb >= (1ll << 32))
+    return fail(FI_E_SHAPE, fn, "K/V strides must be below 4 GiB");
   if ((kv->stride_page * eb) % 16 || (kv->stride_token * eb) % 16 || (kv->stride_head * eb) % 16)
     return fail(FI_E_ARG, fn, "K/V strides must give 16-byte aligned rows (page %lld, token %lld, head %lld elements "
                 "of %d bytes)", (long long)kv->stride_page, (long long)kv->stride_token, (long long)kv->stride_head, eb);

@@ -188,6 +188,10 @@ __device__ __forceinline__ uint16_t to_bits(float a) {
 }
 
 // Cross-lane max / sum over lanes l, l^16, l^32, l^48 (ds_swizzle-free: bpermute).
+// A value the caller knows to be equal on every lane of the wave, moved to a
+// scalar register so that branches on it are scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask); }
 

@@ -11,16 +11,33 @@
 // block of query tokens); every wave holds 32 query rows of one q head, so the
 // 4 waves share each K/V tile (GQA packing: one tile serves up to 4 q heads).
 // Per 64-token K/V tile:
-//   * the workgroup gathers the tile's rows from their pages, widens fp8 to
-//     q's type in registers and stores a 2-byte tile in LDS -- the
-//     dequantize-on-load design the PR describes (Kernel; Architecture /
-//     design notes), here with 16-byte loads per lane, which the PR's Known
-//     limitations name as what its 4-byte loads lacked;
-//   * each wave computes S^T = K Q^T on MFMA 32x32x16 (tokens x rows), masks,
-//     runs the online softmax in base 2 and accumulates O^T += V^T P^T, the
-//     probabilities feeding the MFMA straight from the S^T registers; the
-//     log-sum-exp comes from the sum of the fp32 probabilities, the output is
-//     normalised by the sum of the rounded ones the MFMA applied.
+//   * the workgroup gathers the tile's rows from their pages with coalesced
+//     16-byte loads (8 lanes per 128-byte fp8 row), two tiles ahead, widens
+//     fp8 to q's type in registers and stores 2-byte K and V tiles in LDS --
+//     the dequantize-on-load design the PR describes (Kernel; Architecture /
+//     design notes), with the wide loads its Known limitations ask for.
+//     The LDS traffic is laid out to be free of bank conflicts (measured with
+//     the SQ_LDS_BANK_CONFLICT counter on gfx950): each row's stores are two
+//     contiguous 128-byte runs (the fp8 head dimensions are permuted to make
+//     them so; Q is loaded in the same order and the output undoes it), the K
+//     pitch is 16 mod 256 bytes for the 16-byte reads of 32 rows, and the V
+//     pitch 64 mod 256 bytes for the transposed reads of 4 rows x 32 bytes,
+//     which then take 2 cycles each; every read address is a per-lane base
+//     plus a compile-time offset;
+//   * each wave computes S^T = K Q^T on MFMA 32x32x16 (tokens x rows), runs
+//     the online softmax in base 2 and accumulates O^T += V^T P^T, the
+//     probabilities feeding the MFMA straight from the S^T registers and V
+//     gathered column-wise by ds_read_b64_tr_b16;
+//   * the softmax is kept lean: the mask is applied only on tiles that cross
+//     the causal diagonal or the end of the sequence; the logit scale and the
+//     running max enter exp2 through one FMA; the output accumulator is
+//     rescaled only when a row max grows by more than 2^8 (the exponents stay
+//     below 2^8, so nothing overflows, and the final division by the same sum
+//     makes the result independent of when the max was taken).
+// The row sums of the probabilities as rounded for the PV MFMA come from the
+// MFMA itself (an all-ones operand against P^T), exact in fp32; they normalise
+// the output and, for fp16 (rounding 2^-11), give the log-sum-exp.  With a
+// bf16 query (rounding 2^-9) the log-sum-exp uses a separate fp32 sum.
 #include "fi_device.hpp"
 
 namespace fi {
@@ -28,29 +45,33 @@ namespace fi {
 template <bool QBF16, int KVF, bool OBF16, int D>
 struct PrefillCfg {
   static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
+  static constexpr bool kF32Sum = QBF16;        // bf16 probabilities round at 2^-9: LSE from an fp32 sum
   static constexpr int KVB = kFp8 ? 1 : 2;
-  static constexpr int TK = 64;              // keys per tile
-  static constexpr int KP = D * 2 + 16;      // LDS row pitch (bytes) of the 2-byte tiles
-  static constexpr int FILL_E = D / 4;       // elements each thread moves per tile row
-  static constexpr int FILL_U = FILL_E * KVB / 16;  // 16-byte loads per thread per tensor
-  static constexpr int NS = D / 16;          // QK k-steps (MFMA k = 16)
-  static constexpr int NDB = D / 32;         // PV head_dim blocks of 32
-  static constexpr int LDS = 2 * TK * KP;
-};
-
-template <bool QBF16, int KVF, int D>
-struct TileRegs {
-  using Cfg = PrefillCfg<QBF16, KVF, false, D>;
-  uint4 k[Cfg::FILL_U];
-  uint4 v[Cfg::FILL_U];
+  static constexpr int TK = 64;                 // keys per tile
+  static constexpr int DB = D * KVB;            // stored bytes of a row
+  static constexpr int ROW = D * 2;             // bytes of a 2-byte row
+  static constexpr int KP = ROW + 16;           // K tile pitch, 16 mod 256 bytes
+  static constexpr int VP = (ROW + 191) / 256 * 256 + 64;  // V tile pitch, 64 mod 256 bytes
+  static constexpr int KTILE = TK * KP;
+  static constexpr int STAGE = KTILE + TK * VP; // K then V
+  static constexpr int PER = TK * DB / (16 * 256);  // 16-byte global loads per thread per tensor
+  static constexpr int NS = D / 16;             // QK k-steps (MFMA k = 16)
+  static constexpr int NDB = D / 32;            // PV head_dim blocks of 32
+  static constexpr int LDS = 2 * STAGE;
+  // Head-dimension order of the LDS tiles.  An fp8 lane holds 16 consecutive
+  // dimensions (16c .. 16c+15) and stores their widened halves 128 bytes
+  // apart, so the 8 lanes of a row write two contiguous 128-byte runs: tile
+  // position p holds dimension dim_of(p).  2-byte tiles keep the natural order.
+  __host__ __device__ static constexpr int dim_of(int p) {
+    if (!kFp8) return p;
+    return p < D / 2 ? 16 * (p / 8) + p % 8 : 16 * ((p - D / 2) / 8) + 8 + (p - D / 2) % 8;
+  }
 };
 
 template <bool QBF16, int KVF, bool OBF16, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
   using Cfg = PrefillCfg<QBF16, KVF, OBF16, D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
-  uint8_t* ks = smem;
-  uint8_t* vs = smem + Cfg::TK * Cfg::KP;
 
   const int nsg = p.group / p.heads_per_wg;
   const int x = blockIdx.x;
@@ -59,186 +80,240 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   const int b = x / (nsg * p.num_kv_heads);
   const int qb = p.n_qblocks - 1 - blockIdx.y;  // heaviest (latest) query blocks first
 
-  const int q_begin = p.qo_indptr[b];
-  const int qo_len = p.qo_indptr[b + 1] - q_begin;
+  // request geometry: uniform over the workgroup, kept in scalar registers so
+  // that the tile loop and its branches stay scalar
+  const int q_begin = uniform(p.qo_indptr[b]);
+  const int qo_len = uniform(p.qo_indptr[b + 1]) - q_begin;
   const int q0 = qb * p.q_per_wg;
   if (q0 >= qo_len) return;
-  const int a = p.indptr[b], e = p.indptr[b + 1];
-  const int kv_len = (e > a) ? (e - a - 1) * p.page_size + p.last_page_len[b] : 0;
+  const int a = uniform(p.indptr[b]), e = uniform(p.indptr[b + 1]);
+  const int kv_len = (e > a) ? (e - a - 1) * p.page_size + uniform(p.last_page_len[b]) : 0;
   const int prefix = kv_len - qo_len;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);
   const int lane = tid & 63;
   const int rho = lane & 31;
   const int hh = lane >> 5;
   const int head_local = w % p.heads_per_wg;
   const int tsub = w / p.heads_per_wg;
   const int hq = g * p.group + sg * p.heads_per_wg + head_local;
-  const int qpos = q0 + 32 * tsub + rho;  // this lane's query row
+  const int qw0 = q0 + 32 * tsub;         // this wave's first query row
+  const int qpos = qw0 + rho;             // this lane's query row
   const bool row_ok = qpos < qo_len;
 
-  // last key any row of the workgroup can see
+  // keys the workgroup needs, and the keys every / some row of this wave sees
   const int q_last = min(q0 + p.q_per_wg, qo_len) - 1;
   const int key_end = p.causal ? min(kv_len, q_last + prefix + 1) : kv_len;
-  const int ntiles = (key_end > 0) ? (key_end + Cfg::TK - 1) / Cfg::TK : 0;
-  // last key this lane's row can see (exclusive bound)
+  const int ntiles = uniform((key_end > 0) ? (key_end + Cfg::TK - 1) / Cfg::TK : 0);
   const int row_key_end = p.causal ? min(kv_len, qpos + prefix + 1) : kv_len;
+  const int wave_full_end = uniform(p.causal ? min(kv_len, qw0 + prefix + 1) : kv_len);  // all rows see keys below
+  const int wave_any_end =
+      uniform(p.causal ? min(kv_len, min(qw0 + 31, qo_len - 1) + prefix + 1) : kv_len);  // no row sees keys at or above
+  const bool wave_ok = qw0 < qo_len;
 
-  // Q^T operand: lane (hh, rho) holds q[row rho][(D/2)*hh + 8s + j].
+  // Q^T operand: lane (hh, rho) holds q[row rho] at the dimensions of K tile
+  // positions (D/2)*hh + 8s + j, j = 0..7 (8 consecutive dimensions).
   uint4 qop[Cfg::NS];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
-                                                     ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D +
-                                                     (D / 2) * hh);
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D;
 #pragma unroll
-    for (int s = 0; s < Cfg::NS; ++s) qop[s] = row_ok ? qp[s] : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < Cfg::NS; ++s)
+      qop[s] = row_ok ? *reinterpret_cast<const uint4*>(qp + Cfg::dim_of((D / 2) * hh + 8 * s)) : make_uint4(0, 0, 0, 0);
   }
 
-  // transposed-read address of this lane for the V^T operand: within each
-  // 16-lane group, lanes 4r..4r+3 name the four 8-byte pieces of row r
-  const uint8_t* v_tr = vs + (4 * hh + ((rho & 15) >> 2)) * Cfg::KP + (16 * (rho >> 4) + 4 * (rho & 3)) * 2;
-
-  // tile fill: thread -> (token row = tid / 4, element range part * D/4)
-  const int f_tok = tid >> 2;
-  const int f_part = tid & 3;
-  const uint8_t* kb = p.k + (int64_t)g * p.sh + f_part * Cfg::FILL_E * Cfg::KVB;
-  const uint8_t* vb = p.v + (int64_t)g * p.sh + f_part * Cfg::FILL_E * Cfg::KVB;
-
-  auto load_pid = [&](int tile) -> int {
-    const int t = min(tile * Cfg::TK + f_tok, max(kv_len - 1, 0));
-    return p.indices[a + (t >> p.page_shift)];
+  // tile loads: chunk ci = j*256 + tid of a tensor's tile is row ci / (DB/16),
+  // 16-byte column ci % (DB/16); 8 lanes read one 128-byte fp8 row
+  constexpr int SC = Cfg::DB / 16;  // stored 16-byte chunks per row
+  int ld_row[Cfg::PER], ld_col[Cfg::PER];
+#pragma unroll
+  for (int j = 0; j < Cfg::PER; ++j) {
+    const int ci = j * 256 + tid;
+    ld_row[j] = ci / SC;
+    ld_col[j] = ci % SC;
+  }
+  const uint8_t* kb = p.k + (int64_t)g * p.sh;
+  const uint8_t* vb = p.v + (int64_t)g * p.sh;
+  // One register set per LDS stage: the tile's data and the page ids of the
+  // tile two loads later.  Page ids are fetched a whole tile ahead of the data
+  // they address, so waiting for them never waits for the data loads issued
+  // after them (vector memory counters retire in order).
+  struct Regs {
+    uint4 k[Cfg::PER];
+    uint4 v[Cfg::PER];
+    uint32_t pid[Cfg::PER];
   };
-  auto issue = [&](int tile, int pid, TileRegs<QBF16, KVF, D>& r) {
-    const int t = min(tile * Cfg::TK + f_tok, max(kv_len - 1, 0));
-    const int64_t off = (int64_t)pid * p.sp + (int64_t)(t & (p.page_size - 1)) * p.st;
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + off);
-    const uint4* vp = reinterpret_cast<const uint4*>(vb + off);
+  auto row_token = [&](int tile, int j) { return min(tile * Cfg::TK + ld_row[j], max(kv_len - 1, 0)); };
+  auto load_pids = [&](int tile, Regs& r) {
 #pragma unroll
-    for (int u = 0; u < Cfg::FILL_U; ++u) r.k[u] = kp[u];
-#pragma unroll
-    for (int u = 0; u < Cfg::FILL_U; ++u) r.v[u] = vp[u];
+    for (int j = 0; j < Cfg::PER; ++j) r.pid[j] = (uint32_t)p.indices[a + (row_token(tile, j) >> p.page_shift)];
   };
-  // widen into q's type and store the row slice into the LDS tiles
-  auto store = [&](int tile, TileRegs<QBF16, KVF, D>& r) {
-    const bool ok = tile * Cfg::TK + f_tok < kv_len;
-    uint4* kd = reinterpret_cast<uint4*>(ks + f_tok * Cfg::KP + f_part * Cfg::FILL_E * 2);
-    uint4* vd = reinterpret_cast<uint4*>(vs + f_tok * Cfg::KP + f_part * Cfg::FILL_E * 2);
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    if constexpr (Cfg::kFp8) {
+  auto load_tile = [&](int tile, Regs& r) {
 #pragma unroll
-      for (int u = 0; u < Cfg::FILL_U; ++u) {
-        kd[2 * u] = ok ? widen8<QBF16, KVF>(r.k[u].x, r.k[u].y) : z;
-        kd[2 * u + 1] = ok ? widen8<QBF16, KVF>(r.k[u].z, r.k[u].w) : z;
-        vd[2 * u] = ok ? widen8<QBF16, KVF>(r.v[u].x, r.v[u].y) : z;
-        vd[2 * u + 1] = ok ? widen8<QBF16, KVF>(r.v[u].z, r.v[u].w) : z;
-      }
-    } else {
+    for (int j = 0; j < Cfg::PER; ++j) {
+      const int t = row_token(tile, j);
+      const uint64_t off = (uint64_t)r.pid[j] * (uint32_t)p.sp +
+                           (uint32_t)((t & (p.page_size - 1)) * (uint32_t)p.st) + (uint32_t)(ld_col[j] * 16);
+      r.k[j] = load16(kb + off);
+      r.v[j] = load16(vb + off);
+    }
+  };
+  // widen into q's type and store into an LDS stage.  Rows past kv_len hold
+  // the last valid token again (row_token clamps): finite values whose keys
+  // the mask sets to -inf, so their probabilities are exactly 0.
+  auto store_tile = [&](Regs& r, uint8_t* stage) {
 #pragma unroll
-      for (int u = 0; u < Cfg::FILL_U; ++u) {
-        kd[u] = ok ? r.k[u] : z;
-        vd[u] = ok ? r.v[u] : z;
+    for (int j = 0; j < Cfg::PER; ++j) {
+      const int row = ld_row[j];
+      const uint4 kx = r.k[j], vx = r.v[j];
+      uint8_t* kd = stage + row * Cfg::KP;
+      uint8_t* vd = stage + Cfg::KTILE + row * Cfg::VP;
+      if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
+        const int c0 = 16 * ld_col[j];
+        *reinterpret_cast<uint4*>(kd + c0) = widen8<QBF16, KVF>(kx.x, kx.y);
+        *reinterpret_cast<uint4*>(kd + D + c0) = widen8<QBF16, KVF>(kx.z, kx.w);
+        *reinterpret_cast<uint4*>(vd + c0) = widen8<QBF16, KVF>(vx.x, vx.y);
+        *reinterpret_cast<uint4*>(vd + D + c0) = widen8<QBF16, KVF>(vx.z, vx.w);
+      } else {
+        *reinterpret_cast<uint4*>(kd + 16 * ld_col[j]) = kx;
+        *reinterpret_cast<uint4*>(vd + 16 * ld_col[j]) = vx;
       }
     }
   };
 
-  float m_run = kNegInf;
-  float l_run = 0.f;   // sum of fp32 probabilities (log-sum-exp)
-  float lr_run = 0.f;  // sum of the probabilities rounded to q's type (output normalisation)
+  float m_run = kNegInf;  // running max (base-2 scaled logits), updated lazily
+  float l_run = 0.f;      // sum of fp32 probabilities (bf16 only)
   f32x16_t acc[Cfg::NDB];
+  f32x16_t accs;          // row sums of the rounded probabilities (every element of a lane alike)
 #pragma unroll
   for (int i = 0; i < Cfg::NDB; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) accs[j] = 0.f;
+  const uint32_t one2 = QBF16 ? 0x3f803f80u : 0x3c003c00u;  // two 1.0 in the MFMA type
+  const uint4 ones = make_uint4(one2, one2, one2, one2);
 
-  auto compute = [&](int tile) {
+  // per-lane LDS read bases (stage 0); everything else is a constant offset.
+  // K: lane (hh, rho) reads row 32*sub + rho, bytes [D*hh + 16*st, +16).
+  // V^T transposed reads: within each 16-lane group (same hh, same rho / 16),
+  // lanes 4r..4r+3 name the four 8-byte pieces of row r of a 16-column block.
+  const int k_base = rho * Cfg::KP + D * hh;
+  const int v_base = Cfg::KTILE + (4 * hh + ((rho & 15) >> 2)) * Cfg::VP + 32 * (rho >> 4) + 8 * (rho & 3);
+
+  auto compute = [&](int tile, const uint8_t* stage) {
     const int kbase = tile * Cfg::TK;
+    if (kbase >= wave_any_end) return;  // no row of this wave sees this tile
+    const uint8_t* kl = stage + k_base;
+    const uint8_t* vl = stage + v_base;
     // S^T = K Q^T, two 32-token halves
     f32x16_t s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[sub][j] = 0.f;
-      const uint8_t* krow = ks + (32 * sub + rho) * Cfg::KP + D * hh;
 #pragma unroll
       for (int st = 0; st < Cfg::NS; ++st) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(krow + 16 * st);
+        const uint4 kop = *reinterpret_cast<const uint4*>(kl + 32 * sub * Cfg::KP + 16 * st);
         s[sub] = mfma32x32x16<QBF16>(kop, qop[st], s[sub]);
       }
     }
-    // mask + online softmax; lane holds keys 32*sub + 8*(i/4) + 4*hh + i%4
-    float bm = kNegInf;
+    // lane (hh, rho) holds keys kbase + 32*sub + 8*(i/4) + 4*hh + i%4 of row rho
+    if (kbase + Cfg::TK > wave_full_end) {  // the tile crosses the diagonal or the end
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = kbase + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (t >= row_key_end) s[sub][i] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = kbase + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const float v = (t < row_key_end) ? s[sub][i] * p.scale_log2 : kNegInf;
-        s[sub][i] = v;
-        bm = fmaxf(bm, v);
-      }
-    bm = xor_max(bm, 32);
-    const float m_new = fmaxf(m_run, bm);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[sub][i], s[sub][i + 1]));
+    mx = xor_max(mx, 32) * p.scale_log2;  // base-2 logits (scale > 0 keeps the order)
+    // lazy rescale: move the reference max only when some row's max grows by
+    // more than 8 (log2) -- then exp2 stays below 2^8
+    const bool grow = mx > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      if constexpr (Cfg::kF32Sum) l_run *= alpha;
+      accs *= alpha;
+#pragma unroll
+      for (int i = 0; i < Cfg::NDB; ++i) acc[i] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     uint4 pop[4];
-    float psum = 0.f, prsum = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t wds[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int i0 = 8 * (u & 1) + 2 * jj;
-        const float e0 = fast_exp2(s[u >> 1][i0] - m_use), e1 = fast_exp2(s[u >> 1][i0 + 1] - m_use);
+        const float e0 = fast_exp2(__builtin_fmaf(s[u >> 1][i0], p.scale_log2, -m_use));
+        const float e1 = fast_exp2(__builtin_fmaf(s[u >> 1][i0 + 1], p.scale_log2, -m_use));
         wds[jj] = pack2<QBF16>(e0, e1);
-        const float2 f = unpack2<QBF16>(wds[jj]);
-        prsum += f.x + f.y;
-        psum += e0 + e1;
+        if constexpr (Cfg::kF32Sum) psum += e0 + e1;
       }
       pop[u] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+      accs = mfma32x32x16<QBF16>(ones, pop[u], accs);
     }
-    l_run = l_run * alpha + psum;
-    lr_run = lr_run * alpha + prsum;
-#pragma unroll
-    for (int i = 0; i < Cfg::NDB; ++i) acc[i] *= alpha;
+    if constexpr (Cfg::kF32Sum) l_run += psum;
     // O^T += V^T P^T.  Lane (hh, rho) needs column 32*db + rho of the V tile
     // over tokens r0..r0+3 and r0+8..r0+11 (r0 = 32*(u/2) + 16*(u%2) + 4*hh),
     // the order its P^T slots hold: two transposed LDS reads of 4 rows each.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r0 = 32 * (u >> 1) + 16 * (u & 1);
-      const uint8_t* a1 = v_tr + r0 * Cfg::KP;
-      const uint8_t* a2 = a1 + 8 * Cfg::KP;
+      const uint8_t* a1 = vl + (32 * (u >> 1) + 16 * (u & 1)) * Cfg::VP;
 #pragma unroll
       for (int db = 0; db < Cfg::NDB; ++db) {
         const uint2 x1 = lds_tr16(a1 + 64 * db);
-        const uint2 x2 = lds_tr16(a2 + 64 * db);
+        const uint2 x2 = lds_tr16(a1 + 8 * Cfg::VP + 64 * db);
         acc[db] = mfma32x32x16<QBF16>(make_uint4(x1.x, x1.y, x2.x, x2.y), pop[u], acc[db]);
       }
     }
   };
 
+  // two LDS stages, tile loads two tiles ahead (page ids four), one barrier per tile (it
+  // publishes the stage just written and tells the writer of the other stage
+  // that its previous readers are done); past the last tile the index is
+  // clamped, so the extra loads re-read cached lines
   if (ntiles > 0) {
-    TileRegs<QBF16, KVF, D> ra;
-    int pid = load_pid(0);
-    issue(0, pid, ra);
-    int pid_next = load_pid(min(1, ntiles - 1));
-    for (int tile = 0; tile < ntiles; ++tile) {
-      store(tile, ra);
+    auto tile_of = [&](int k) { return min(k, ntiles - 1); };
+    Regs ra, rb;
+    load_pids(0, ra);
+    load_pids(tile_of(1), rb);
+    load_tile(0, ra);
+    load_pids(tile_of(2), ra);
+    load_tile(tile_of(1), rb);
+    load_pids(tile_of(3), rb);
+    // Tiles go in pairs and both halves always load (an odd count re-reads
+    // the last tile once), so every path round the loop issues the same
+    // loads and the memory waits stay one tile deep.
+    for (int k = 0; k < ntiles; k += 2) {
+      store_tile(ra, smem);
+      load_tile(tile_of(k + 2), ra);
+      load_pids(tile_of(k + 4), ra);
       __syncthreads();
-      if (tile + 1 < ntiles) {
-        issue(tile + 1, pid_next, ra);
-        pid_next = load_pid(min(tile + 2, ntiles - 1));
-      }
-      compute(tile);
+      if (wave_ok) compute(k, smem);
+      store_tile(rb, smem + Cfg::STAGE);
+      load_tile(tile_of(k + 3), rb);
+      load_pids(tile_of(k + 5), rb);
       __syncthreads();
+      if (wave_ok && k + 1 < ntiles) compute(k + 1, smem + Cfg::STAGE);
     }
   }
 
   // epilogue
-  l_run = xor_sum(l_run, 32);
-  lr_run = xor_sum(lr_run, 32);
+  const float lr_run = accs[0];
+  if constexpr (Cfg::kF32Sum) l_run = xor_sum(l_run, 32);
+  else l_run = lr_run;
   if (!row_ok) return;
   const float inv = (lr_run > 0.f) ? p.v_scale / lr_run : 0.f;
   uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(q_begin + qpos) * p.num_qo_heads + hq) * D;
@@ -246,7 +321,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   for (int db = 0; db < Cfg::NDB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = 32 * db + 8 * i4 + 4 * hh;
+      const int d = Cfg::dim_of(32 * db + 8 * i4 + 4 * hh);  // 4 positions, 4 consecutive dimensions
       *reinterpret_cast<uint2*>(op + d) = make_uint2(pack2<OBF16>(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv),
                                                      pack2<OBF16>(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv));
     }
