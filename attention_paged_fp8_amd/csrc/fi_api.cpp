@@ -445,7 +445,7 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   p.num_kv_heads = kv->num_kv_heads;
   p.group = num_qo_heads / kv->num_kv_heads;
   p.heads_per_wg = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
-  p.q_per_wg = 128 / p.heads_per_wg;
+  p.q_per_wg = 32 * fi::kPrefillWaves / p.heads_per_wg;
   p.n_qblocks = (int32_t)ceil_div(max_qo, p.q_per_wg);
   p.causal = causal ? 1 : 0;
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)kv->head_dim);

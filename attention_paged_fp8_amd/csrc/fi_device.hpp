@@ -168,6 +168,19 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
+// c + w.lo + w.hi for a packed pair of 2-byte values, summed in fp32
+// (v_dot2_f32_{f16,bf16} against (1, 1): the products are exact)
+template <bool BF16>
+__device__ __forceinline__ float sum2(uint32_t w, float c) {
+  if constexpr (BF16) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(w), one, c, false);
+  } else {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(bitcast<f16x2_t>(w), one, c, false);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float2 unpack2(uint32_t w) {
   if constexpr (BF16) {
@@ -191,6 +204,19 @@ __device__ __forceinline__ uint16_t to_bits(float a) {
 // A value the caller knows to be equal on every lane of the wave, moved to a
 // scalar register so that branches on it are scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Max / sum of v and v from the lane 32 away, through v_permlane32_swap (a
+// register exchange between the wave's halves: no LDS round trip).  With both
+// operands v, the two results are v and its partner in the same order on
+// every lane, so both halves compute the identical value.
+__device__ __forceinline__ float max_half_swap(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_half_swap(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask); }

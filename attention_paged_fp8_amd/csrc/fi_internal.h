@@ -68,6 +68,9 @@ struct MergeParams {
   float v_scale;
 };
 
+// Prefill workgroups: waves of 32 query rows sharing each K/V tile.
+constexpr int kPrefillWaves = 8;
+
 struct PrefillParams {
   const void* q;          // [total_q, Hqo, D]
   void* o;

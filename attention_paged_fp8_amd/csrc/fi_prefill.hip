@@ -7,12 +7,13 @@
 // PR #368: Summary, Kernel, Benchmark results).  The causal mask is aligned to
 // the end of the KV sequence: row r sees key t iff t <= r + kv_len - qo_len.
 //
-// Mapping.  A workgroup of 4 waves owns one (request, kv head, group of heads,
+// Mapping.  A workgroup of 8 waves owns one (request, kv head, group of heads,
 // block of query tokens); every wave holds 32 query rows of one q head, so the
-// 4 waves share each K/V tile (GQA packing: one tile serves up to 4 q heads).
+// 8 waves (256 rows, up to 4 q heads of a GQA group) share each K/V tile and
+// its gather, widening and LDS stores.
 // Per 64-token K/V tile:
 //   * the workgroup gathers the tile's rows from their pages with coalesced
-//     16-byte loads (8 lanes per 128-byte fp8 row), two tiles ahead, widens
+//     16-byte loads (8 lanes per 128-byte fp8 row), four tiles ahead, widens
 //     fp8 to q's type in registers and stores 2-byte K and V tiles in LDS --
 //     the dequantize-on-load design the PR describes (Kernel; Architecture /
 //     design notes), with the wide loads its Known limitations ask for.
@@ -34,10 +35,13 @@
 //     rescaled only when a row max grows by more than 2^8 (the exponents stay
 //     below 2^8, so nothing overflows, and the final division by the same sum
 //     makes the result independent of when the max was taken).
-// The row sums of the probabilities as rounded for the PV MFMA come from the
-// MFMA itself (an all-ones operand against P^T), exact in fp32; they normalise
-// the output and, for fp16 (rounding 2^-11), give the log-sum-exp.  With a
-// bf16 query (rounding 2^-9) the log-sum-exp uses a separate fp32 sum.
+// The row sums of the probabilities as rounded for the PV MFMA are taken
+// with v_dot2 against (1, 1), two values per instruction, exact products and
+// an fp32 sum; they normalise the output and, for fp16 (rounding 2^-11), give
+// the log-sum-exp.  With a bf16 query (rounding 2^-9) the log-sum-exp uses a
+// separate sum of the fp32 values.
+// Each wave also overlaps its two phases: the QK MFMAs of the next tile are
+// issued between the exponentials of the current one.
 #include "fi_device.hpp"
 
 namespace fi {
@@ -45,7 +49,11 @@ namespace fi {
 template <bool QBF16, int KVF, bool OBF16, int D>
 struct PrefillCfg {
   static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
-  static constexpr bool kF32Sum = QBF16;        // bf16 probabilities round at 2^-9: LSE from an fp32 sum
+  // The output is normalised by the sum of the probabilities as rounded for
+  // the PV MFMA.  fp16 rounds at 2^-11 and that sum also gives the
+  // log-sum-exp; bf16 rounds at 2^-9, so its log-sum-exp uses a separate sum
+  // of the fp32 values.
+  static constexpr bool kF32Lse = QBF16;
   static constexpr int KVB = kFp8 ? 1 : 2;
   static constexpr int TK = 64;                 // keys per tile
   static constexpr int DB = D * KVB;            // stored bytes of a row
@@ -53,11 +61,15 @@ struct PrefillCfg {
   static constexpr int KP = ROW + 16;           // K tile pitch, 16 mod 256 bytes
   static constexpr int VP = (ROW + 191) / 256 * 256 + 64;  // V tile pitch, 64 mod 256 bytes
   static constexpr int KTILE = TK * KP;
-  static constexpr int STAGE = KTILE + TK * VP; // K then V
-  static constexpr int PER = TK * DB / (16 * 256);  // 16-byte global loads per thread per tensor
+  static constexpr int VTILE = TK * VP;
+  // two K slots, then two V slots
+  static constexpr int K0 = 0, K1 = KTILE, V0 = 2 * KTILE, V1 = 2 * KTILE + VTILE;
+  static constexpr int LDS = 2 * KTILE + 2 * VTILE;
+  static constexpr int NT = 64 * kPrefillWaves;     // threads per workgroup
+  static constexpr int CHUNKS = TK * DB / 16;       // 16-byte pieces of a tile of one tensor
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;  // per thread (the last round may be partial)
   static constexpr int NS = D / 16;             // QK k-steps (MFMA k = 16)
   static constexpr int NDB = D / 32;            // PV head_dim blocks of 32
-  static constexpr int LDS = 2 * STAGE;
   // Head-dimension order of the LDS tiles.  An fp8 lane holds 16 consecutive
   // dimensions (16c .. 16c+15) and stores their widened halves 128 bytes
   // apart, so the 8 lanes of a row write two contiguous 128-byte runs: tile
@@ -68,8 +80,31 @@ struct PrefillCfg {
   }
 };
 
+// Instruction order for the block that computes S(j+1) = K Q^T while the
+// probabilities of S(j) are formed, then accumulates P V: a few K reads
+// ahead, then each QK MFMA followed by a share of the exponential work and
+// one more LDS read (K, then the V reads of the PV phase), then each PV MFMA
+// with its two transposed reads.
+// (sched_group_barrier masks: 0x008 MFMA, 0x002 VALU, 0x400 transcendental,
+// 0x100 LDS read.)
+template <int NQK, int NPV>
+__device__ __forceinline__ void schedule_overlap() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
 template <bool QBF16, int KVF, bool OBF16, int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const PrefillParams p) {
   using Cfg = PrefillCfg<QBF16, KVF, OBF16, D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
@@ -110,7 +145,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
   const int wave_full_end = uniform(p.causal ? min(kv_len, qw0 + prefix + 1) : kv_len);  // all rows see keys below
   const int wave_any_end =
       uniform(p.causal ? min(kv_len, min(qw0 + 31, qo_len - 1) + prefix + 1) : kv_len);  // no row sees keys at or above
-  const bool wave_ok = qw0 < qo_len;
+  // tiles this wave computes (a prefix of the workgroup's tiles)
+  const int ntw = uniform((qw0 < qo_len && wave_any_end > 0) ? (wave_any_end + Cfg::TK - 1) / Cfg::TK : 0);
 
   // Q^T operand: lane (hh, rho) holds q[row rho] at the dimensions of K tile
   // positions (D/2)*hh + 8s + j, j = 0..7 (8 consecutive dimensions).
@@ -123,92 +159,95 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
       qop[s] = row_ok ? *reinterpret_cast<const uint4*>(qp + Cfg::dim_of((D / 2) * hh + 8 * s)) : make_uint4(0, 0, 0, 0);
   }
 
-  // tile loads: chunk ci = j*256 + tid of a tensor's tile is row ci / (DB/16),
-  // 16-byte column ci % (DB/16); 8 lanes read one 128-byte fp8 row
-  constexpr int SC = Cfg::DB / 16;  // stored 16-byte chunks per row
+  // ---- tile gather ---------------------------------------------------------
+  // Chunk ci = j*NT + tid of a tensor's tile is row ci / (DB/16), 16-byte
+  // column ci % (DB/16): 8 lanes read one 128-byte fp8 row (whole waves sit
+  // out a partial last round).  Rows past kv_len re-read the last valid token
+  // (finite values whose keys the mask sets to -inf, so their probabilities
+  // are exactly 0).
+  constexpr int SC = Cfg::DB / 16;
   int ld_row[Cfg::PER], ld_col[Cfg::PER];
 #pragma unroll
   for (int j = 0; j < Cfg::PER; ++j) {
-    const int ci = j * 256 + tid;
+    const int ci = j * Cfg::NT + tid;
     ld_row[j] = ci / SC;
     ld_col[j] = ci % SC;
   }
+  // does round j of this thread hold a chunk? (uniform per wave)
+  auto ld_on = [&](int j) { return Cfg::CHUNKS % Cfg::NT == 0 || j * Cfg::NT + w * 64 < Cfg::CHUNKS; };
   const uint8_t* kb = p.k + (int64_t)g * p.sh;
   const uint8_t* vb = p.v + (int64_t)g * p.sh;
-  // One register set per LDS stage: the tile's data and the page ids of the
-  // tile two loads later.  Page ids are fetched a whole tile ahead of the data
-  // they address, so waiting for them never waits for the data loads issued
-  // after them (vector memory counters retire in order).
-  struct Regs {
-    uint4 k[Cfg::PER];
-    uint4 v[Cfg::PER];
-    uint32_t pid[Cfg::PER];
+  // a tile's K and V on their way from memory to LDS
+  struct Fetch {
+    uint4 k[Cfg::PER], v[Cfg::PER];
   };
+  uint64_t goff[Cfg::PER];  // byte offsets of this thread's rows of the tile being fetched
+  auto tile_of = [&](int t) { return min(t, ntiles - 1); };
   auto row_token = [&](int tile, int j) { return min(tile * Cfg::TK + ld_row[j], max(kv_len - 1, 0)); };
-  auto load_pids = [&](int tile, Regs& r) {
+  auto load_pids = [&](int tile, uint32_t(&pid)[Cfg::PER]) {
 #pragma unroll
-    for (int j = 0; j < Cfg::PER; ++j) r.pid[j] = (uint32_t)p.indices[a + (row_token(tile, j) >> p.page_shift)];
+    for (int j = 0; j < Cfg::PER; ++j)
+      if (ld_on(j)) pid[j] = (uint32_t)p.indices[a + (row_token(tile, j) >> p.page_shift)];
   };
-  auto load_tile = [&](int tile, Regs& r) {
+  auto offset = [&](int tile, int j, uint32_t pid) -> uint64_t {
+    const int t = row_token(tile, j);
+    return (uint64_t)pid * (uint32_t)p.sp + (uint32_t)((t & (p.page_size - 1)) * (uint32_t)p.st) +
+           (uint32_t)(ld_col[j] * 16);
+  };
+  auto locate = [&](int tile, const uint32_t(&pid)[Cfg::PER]) {
+#pragma unroll
+    for (int j = 0; j < Cfg::PER; ++j)
+      if (ld_on(j)) goff[j] = offset(tile, j, pid[j]);
+  };
+  auto load_k = [&](Fetch& f) {
+#pragma unroll
+    for (int j = 0; j < Cfg::PER; ++j)
+      if (ld_on(j)) f.k[j] = load16(kb + goff[j]);
+  };
+  auto load_v = [&](Fetch& f) {
+#pragma unroll
+    for (int j = 0; j < Cfg::PER; ++j)
+      if (ld_on(j)) f.v[j] = load16(vb + goff[j]);
+  };
+  // widen into q's type and store rows into an LDS slot; fp8 dimensions
+  // 16c..16c+7 go to position 8c and 16c+8..16c+15 to D/2 + 8c
+  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch) {
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j) {
-      const int t = row_token(tile, j);
-      const uint64_t off = (uint64_t)r.pid[j] * (uint32_t)p.sp +
-                           (uint32_t)((t & (p.page_size - 1)) * (uint32_t)p.st) + (uint32_t)(ld_col[j] * 16);
-      r.k[j] = load16(kb + off);
-      r.v[j] = load16(vb + off);
-    }
-  };
-  // widen into q's type and store into an LDS stage.  Rows past kv_len hold
-  // the last valid token again (row_token clamps): finite values whose keys
-  // the mask sets to -inf, so their probabilities are exactly 0.
-  auto store_tile = [&](Regs& r, uint8_t* stage) {
-#pragma unroll
-    for (int j = 0; j < Cfg::PER; ++j) {
-      const int row = ld_row[j];
-      const uint4 kx = r.k[j], vx = r.v[j];
-      uint8_t* kd = stage + row * Cfg::KP;
-      uint8_t* vd = stage + Cfg::KTILE + row * Cfg::VP;
-      if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
-        const int c0 = 16 * ld_col[j];
-        *reinterpret_cast<uint4*>(kd + c0) = widen8<QBF16, KVF>(kx.x, kx.y);
-        *reinterpret_cast<uint4*>(kd + D + c0) = widen8<QBF16, KVF>(kx.z, kx.w);
-        *reinterpret_cast<uint4*>(vd + c0) = widen8<QBF16, KVF>(vx.x, vx.y);
-        *reinterpret_cast<uint4*>(vd + D + c0) = widen8<QBF16, KVF>(vx.z, vx.w);
+      if (!ld_on(j)) continue;
+      uint8_t* d = slot + ld_row[j] * pitch;
+      if constexpr (Cfg::kFp8) {
+        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].x, r[j].y);
+        *reinterpret_cast<uint4*>(d + D + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].z, r[j].w);
       } else {
-        *reinterpret_cast<uint4*>(kd + 16 * ld_col[j]) = kx;
-        *reinterpret_cast<uint4*>(vd + 16 * ld_col[j]) = vx;
+        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = r[j];
       }
     }
   };
+  auto store_k = [&](const Fetch& f, uint8_t* slot) { store_rows(f.k, slot, Cfg::KP); };
+  auto store_v = [&](const Fetch& f, uint8_t* slot) { store_rows(f.v, slot, Cfg::VP); };
 
+  // ---- per-wave attention state --------------------------------------------
   float m_run = kNegInf;  // running max (base-2 scaled logits), updated lazily
-  float l_run = 0.f;      // sum of fp32 probabilities (bf16 only)
+  float lr_run = 0.f;     // this lane's share of the sum of rounded probabilities
+  float l_run = 0.f;      // bf16: this lane's share of the fp32 probability sum
   f32x16_t acc[Cfg::NDB];
-  f32x16_t accs;          // row sums of the rounded probabilities (every element of a lane alike)
 #pragma unroll
   for (int i = 0; i < Cfg::NDB; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) accs[j] = 0.f;
-  const uint32_t one2 = QBF16 ? 0x3f803f80u : 0x3c003c00u;  // two 1.0 in the MFMA type
-  const uint4 ones = make_uint4(one2, one2, one2, one2);
 
-  // per-lane LDS read bases (stage 0); everything else is a constant offset.
+  // per-lane LDS read bases within a slot; everything else is a constant offset.
   // K: lane (hh, rho) reads row 32*sub + rho, bytes [D*hh + 16*st, +16).
   // V^T transposed reads: within each 16-lane group (same hh, same rho / 16),
   // lanes 4r..4r+3 name the four 8-byte pieces of row r of a 16-column block.
   const int k_base = rho * Cfg::KP + D * hh;
-  const int v_base = Cfg::KTILE + (4 * hh + ((rho & 15) >> 2)) * Cfg::VP + 32 * (rho >> 4) + 8 * (rho & 3);
+  const int v_base = (4 * hh + ((rho & 15) >> 2)) * Cfg::VP + 32 * (rho >> 4) + 8 * (rho & 3);
 
-  auto compute = [&](int tile, const uint8_t* stage) {
-    const int kbase = tile * Cfg::TK;
-    if (kbase >= wave_any_end) return;  // no row of this wave sees this tile
-    const uint8_t* kl = stage + k_base;
-    const uint8_t* vl = stage + v_base;
-    // S^T = K Q^T, two 32-token halves
-    f32x16_t s[2];
+  // S^T = K Q^T for one tile, two 32-token halves; lane (hh, rho) then holds
+  // keys 32*sub + 8*(i/4) + 4*hh + i%4 of row rho
+  auto qk = [&](const uint8_t* kslot, f32x16_t(&s)[2]) {
+    const uint8_t* kl = kslot + k_base;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
@@ -219,8 +258,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         s[sub] = mfma32x32x16<QBF16>(kop, qop[st], s[sub]);
       }
     }
-    // lane (hh, rho) holds keys kbase + 32*sub + 8*(i/4) + 4*hh + i%4 of row rho
-    if (kbase + Cfg::TK > wave_full_end) {  // the tile crosses the diagonal or the end
+  };
+  // mask (tiles that cross the diagonal or the end), row max, lazy rescale:
+  // the reference max moves only when some row's max grows by more than 8
+  // (log2), so exp2 stays below 2^8; returns the max the exponents subtract
+  auto softmax_head = [&](int tile, f32x16_t(&s)[2]) -> float {
+    const int kbase = tile * Cfg::TK;
+    if (kbase + Cfg::TK > wave_full_end) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -229,27 +273,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
           if (t >= row_key_end) s[sub][i] = kNegInf;
         }
     }
-    float mx = kNegInf;
+    float mx = fmaxf(s[0][0], s[0][1]);  // then three-operand maxima over pairs
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[sub][i], s[sub][i + 1]));
-    mx = xor_max(mx, 32) * p.scale_log2;  // base-2 logits (scale > 0 keeps the order)
-    // lazy rescale: move the reference max only when some row's max grows by
-    // more than 8 (log2) -- then exp2 stays below 2^8
+    for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(s[i >> 4][i & 15], s[i >> 4][(i & 15) + 1]));
+    mx = max_half_swap(mx) * p.scale_log2;  // base-2 logits (scale > 0 keeps the order)
     const bool grow = mx > m_run + 8.f;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
-      if constexpr (Cfg::kF32Sum) l_run *= alpha;
-      accs *= alpha;
+      lr_run *= alpha;
+      if constexpr (Cfg::kF32Lse) l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < Cfg::NDB; ++i) acc[i] *= alpha;
     }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    uint4 pop[4];
-    float psum = 0.f;
+    return (m_run == kNegInf) ? 0.f : m_run;
+  };
+  // probabilities, rounded to the MFMA type and packed as the P^T operand
+  // (slot u = tokens 16u .. 16u+15), and their row sums
+  auto exp_pack = [&](const f32x16_t(&s)[2], float m_use, uint4(&pop)[4]) {
+    float rsum = 0.f, psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t wds[4];
@@ -259,15 +302,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         const float e0 = fast_exp2(__builtin_fmaf(s[u >> 1][i0], p.scale_log2, -m_use));
         const float e1 = fast_exp2(__builtin_fmaf(s[u >> 1][i0 + 1], p.scale_log2, -m_use));
         wds[jj] = pack2<QBF16>(e0, e1);
-        if constexpr (Cfg::kF32Sum) psum += e0 + e1;
+        rsum = sum2<QBF16>(wds[jj], rsum);
+        if constexpr (Cfg::kF32Lse) psum += e0 + e1;
       }
       pop[u] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-      accs = mfma32x32x16<QBF16>(ones, pop[u], accs);
     }
-    if constexpr (Cfg::kF32Sum) l_run += psum;
-    // O^T += V^T P^T.  Lane (hh, rho) needs column 32*db + rho of the V tile
-    // over tokens r0..r0+3 and r0+8..r0+11 (r0 = 32*(u/2) + 16*(u%2) + 4*hh),
-    // the order its P^T slots hold: two transposed LDS reads of 4 rows each.
+    lr_run += rsum;
+    if constexpr (Cfg::kF32Lse) l_run += psum;
+  };
+  // O^T += V^T P^T.  Lane (hh, rho) needs column 32*db + rho of the V tile
+  // over tokens r0..r0+3 and r0+8..r0+11 (r0 = 32*(u/2) + 16*(u%2) + 4*hh),
+  // the order its P^T slots hold: two transposed LDS reads of 4 rows each.
+  auto pv = [&](const uint8_t* vslot, const uint4(&pop)[4]) {
+    const uint8_t* vl = vslot + v_base;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint8_t* a1 = vl + (32 * (u >> 1) + 16 * (u & 1)) * Cfg::VP;
@@ -280,40 +327,87 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     }
   };
 
-  // two LDS stages, tile loads two tiles ahead (page ids four), one barrier per tile (it
-  // publishes the stage just written and tells the writer of the other stage
-  // that its previous readers are done); past the last tile the index is
-  // clamped, so the extra loads re-read cached lines
+  // ---- the tile pipeline ---------------------------------------------------
+  // Step j: store K(j+2) into the slot K(j) used and fetch K(j+4); mask and
+  // take the row max of S(j); issue S(j+1) = K(j+1) Q^T on the matrix cores
+  // while the same wave turns S(j) into probabilities; accumulate P(j) V(j);
+  // one barrier; store V(j+2) into the slot V(j) used and fetch V(j+4).
+  // K and V each have two LDS slots; the barrier orders every slot's readers
+  // before its next writer and every writer before its readers.  Two register
+  // sets keep tiles in flight two steps ahead; page ids are fetched one step
+  // before the data they address.
+  auto step = [&](int j, f32x16_t(&sc)[2], f32x16_t(&sn)[2], Fetch& f, const uint32_t(&pcur)[Cfg::PER],
+                  uint32_t(&pnext)[Cfg::PER], uint8_t* k_this, const uint8_t* k_next, uint8_t* v_this) {
+    store_k(f, k_this);
+    locate(tile_of(j + 4), pcur);
+    load_k(f);
+    load_pids(tile_of(j + 5), pnext);
+    if (j < ntw) {
+      const float m_use = softmax_head(j, sc);
+      uint4 pop[4];
+      // S(j+1) even past this wave's last tile (the slot then holds a
+      // clamped copy and the result goes unused): no branch splits the
+      // matrix-core work from the exponentials it overlaps
+      qk(k_next, sn);
+      exp_pack(sc, m_use, pop);
+      pv(v_this, pop);
+      schedule_overlap<2 * Cfg::NS, 4 * Cfg::NDB>();
+    }
+    __syncthreads();
+    store_v(f, v_this);
+    load_v(f);
+  };
+
   if (ntiles > 0) {
-    auto tile_of = [&](int k) { return min(k, ntiles - 1); };
-    Regs ra, rb;
-    load_pids(0, ra);
-    load_pids(tile_of(1), rb);
-    load_tile(0, ra);
-    load_pids(tile_of(2), ra);
-    load_tile(tile_of(1), rb);
-    load_pids(tile_of(3), rb);
-    // Tiles go in pairs and both halves always load (an odd count re-reads
-    // the last tile once), so every path round the loop issues the same
-    // loads and the memory waits stay one tile deep.
-    for (int k = 0; k < ntiles; k += 2) {
-      store_tile(ra, smem);
-      load_tile(tile_of(k + 2), ra);
-      load_pids(tile_of(k + 4), ra);
-      __syncthreads();
-      if (wave_ok) compute(k, smem);
-      store_tile(rb, smem + Cfg::STAGE);
-      load_tile(tile_of(k + 3), rb);
-      load_pids(tile_of(k + 5), rb);
-      __syncthreads();
-      if (wave_ok && k + 1 < ntiles) compute(k + 1, smem + Cfg::STAGE);
+    uint8_t* const K0 = smem + Cfg::K0;
+    uint8_t* const K1 = smem + Cfg::K1;
+    uint8_t* const V0 = smem + Cfg::V0;
+    uint8_t* const V1 = smem + Cfg::V1;
+    uint32_t pa[Cfg::PER], pb[Cfg::PER];
+    f32x16_t s0[2], s1[2];
+    Fetch fa, fb;
+    {
+      // tiles 0..3 go out together; 0 and 1 land in LDS, 2 and 3 stay in
+      // the register sets of steps 0 and 1
+      uint32_t q0[Cfg::PER], q1[Cfg::PER], q2[Cfg::PER], q3[Cfg::PER];
+      load_pids(0, q0);
+      load_pids(tile_of(1), q1);
+      load_pids(tile_of(2), q2);
+      load_pids(tile_of(3), q3);
+      load_pids(tile_of(4), pb);
+      Fetch f0, f1;
+      locate(0, q0);
+      load_k(f0);
+      load_v(f0);
+      locate(tile_of(1), q1);
+      load_k(f1);
+      load_v(f1);
+      locate(tile_of(2), q2);
+      load_k(fa);
+      load_v(fa);
+      locate(tile_of(3), q3);
+      load_k(fb);
+      load_v(fb);
+      store_k(f0, K0);
+      store_v(f0, V0);
+      store_k(f1, K1);
+      store_v(f1, V1);
+    }
+    __syncthreads();
+    if (ntw > 0) qk(K0, s0);
+    __syncthreads();  // every wave has read K(0) before step 0 overwrites its slot
+    // Steps go in pairs (the register roles swap) and every step stores,
+    // loads and waits whether or not this wave computes, so every path
+    // round the loop issues the same memory operations.
+    for (int j = 0; j < ntiles; j += 2) {
+      step(j, s0, s1, fa, pb, pa, K0, K1, V0);
+      step(j + 1, s1, s0, fb, pa, pb, K1, K0, V1);
     }
   }
 
-  // epilogue
-  const float lr_run = accs[0];
-  if constexpr (Cfg::kF32Sum) l_run = xor_sum(l_run, 32);
-  else l_run = lr_run;
+  // ---- epilogue ------------------------------------------------------------
+  lr_run = sum_half_swap(lr_run);
+  l_run = Cfg::kF32Lse ? sum_half_swap(l_run) : lr_run;
   if (!row_ok) return;
   const float inv = (lr_run > 0.f) ? p.v_scale / lr_run : 0.f;
   uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(q_begin + qpos) * p.num_qo_heads + hq) * D;
@@ -334,7 +428,7 @@ template <bool QBF16, int KVF, bool OBF16, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, int batch, hipStream_t s) {
   const int nsg = p.group / p.heads_per_wg;
   dim3 grid(batch * p.num_kv_heads * nsg, p.n_qblocks);
-  hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D>), grid, dim3(64 * kPrefillWaves), 0, s, p);
   return hipGetLastError();
 }
 
