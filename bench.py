@@ -21,6 +21,7 @@ and the float64 oracle timed on the host cores on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS_16 = 2500.0   # MI355X dense fp16 / bf16 MFMA
 METRIC = "decode fp8-KV HBM GB/s (% of peak); prefill TFLOP/s (% of MFMA peak)"
@@ -157,6 +159,53 @@ def run_prefill_bench(steps, warmup):
     return w, wall_ms, ev
 
 
+def kernel_source_hash(kind: str) -> str:
+    """sha256 over the sources that define a kernel (its .hip file and the
+    shared device and internal headers)."""
+    csrc = os.path.join(ROOT, "attention_paged_fp8_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (f"fi_{kind}.hip", "fi_device.hpp", "fi_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per call from the committed counter summary
+    profiles/<kind>_kernel.<workload>.traffic.txt (FETCH_SIZE and WRITE_SIZE
+    per dispatch, each scaled by the reading of a plain copy of known size), or
+    None when the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kind}_kernel.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash(kind):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def run_copy_calibration(mb: int, reps: int = 5):
+    """A plain device-to-device copy of `mb` MiB, `reps` times: the reference
+    the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: {reps} copies of {n} bytes", flush=True)
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """The float64 oracle on a bounded sample of the decode workload (whole
     requests, in order, until about budget_s of CPU time), one BLAS thread."""
@@ -189,11 +238,19 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all",
+                    help="run one path only (for per-kernel counter passes)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this library and benchmark run on one GPU only; "
               "multi-GPU sharding is not implemented", file=sys.stderr)
         sys.exit(2)
+
+    if args.calib_copy:
+        run_copy_calibration(args.calib_copy)
+        return
 
     from attention_paged_fp8_amd import fi
 
@@ -201,7 +258,11 @@ def main():
         from attention_paged_fp8_amd.build import build
         build()
 
-    w, wall_ms, ev = run_decode_bench(args.steps, args.warmup, args.copies)
+    from workloads import make_config
+
+    w, wall_ms, ev = make_config(2), float("nan"), np.array([float("nan")])
+    if args.only in ("all", "decode"):
+        w, wall_ms, ev = run_decode_bench(args.steps, args.warmup, args.copies)
     nbytes = decode_bytes(w)
     value = nbytes / (wall_ms * 1e-3) / 1e9
     ev_ms = float(ev.mean())
@@ -209,23 +270,32 @@ def main():
     print(f"# decode: {nbytes / 1e6:.1f} MB per call, wall {wall_ms * 1e3:.1f} us/step, events mean "
           f"{ev_ms * 1e3:.1f} us (min {ev.min() * 1e3:.1f}, max {ev.max() * 1e3:.1f})", file=sys.stderr, flush=True)
 
-    pw, p_wall, p_ev = run_prefill_bench(args.prefill_steps, 3)
-    flops = prefill_flops(pw)
-    p_ms = float(p_ev.mean())
-    tflops = flops / (p_ms * 1e-3) / 1e12
-    print(f"# prefill: {flops / 1e9:.1f} GFLOP per call, events mean {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s",
-          file=sys.stderr, flush=True)
+    prefill = None
+    if args.only in ("all", "prefill"):
+        pw, p_wall, p_ev = run_prefill_bench(args.prefill_steps, 3)
+        flops = prefill_flops(pw)
+        p_ms = float(p_ev.mean())
+        tflops = flops / (p_ms * 1e-3) / 1e12
+        print(f"# prefill: {flops / 1e9:.1f} GFLOP per call, events mean {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        prefill = {
+            "workload": pw["name"], "tflops": round(tflops, 2), "ms": round(p_ms, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS_16,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS_16, 4),
+                         "traffic": measured_traffic("prefill", pw["name"]), "flops_per_launch": flops},
+            "dtype": "f16",
+        }
 
-    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_budget)
+    cpu = None if (args.no_cpu or args.only == "prefill") else cpu_baseline(w, args.cpu_budget)
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(value, 2) if np.isfinite(value) else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 5),
+        "ms_per_step": round(wall_ms, 5) if np.isfinite(wall_ms) else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -238,17 +308,11 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode", w["name"]),
             "kernel": "decode_kernel + merge_kernel (one C-ABI call, timed with HIP events on its stream)",
             "bytes_per_launch": nbytes,
         },
-        "prefill": {
-            "workload": pw["name"], "tflops": round(tflops, 2), "ms": round(p_ms, 5),
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS_16,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS_16, 4), "traffic": None,
-                         "flops_per_launch": flops},
-            "dtype": "f16",
-        },
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
