@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -394,6 +395,34 @@ fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const
                     workspace, workspace_bytes, sm_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
 }
 
+// Dispatch order of causal / full prefill: the (request, query block) pairs
+// sorted by the number of K/V tiles they walk, heaviest first, so that the
+// hardware's in-order dispatch approximates longest-processing-time
+// scheduling and no workgroup is launched for an empty query block.  Left
+// empty (grid order) when the pairs do not fit in the kernel arguments.
+static void plan_prefill_order(fi::PrefillParams& p, int32_t batch, const int32_t* qo_indptr_h, const fi_paged_kv* kv) {
+  p.n_items = 0;
+  if (batch >= 65536) return;
+  int64_t pairs = 0;
+  for (int32_t i = 0; i < batch; ++i) pairs += ceil_div(qo_indptr_h[i + 1] - qo_indptr_h[i], p.q_per_wg);
+  if (pairs > fi::kPrefillOrderMax) return;
+  std::vector<std::pair<int64_t, uint32_t>> items;  // (tiles, request << 16 | block)
+  items.reserve((size_t)pairs);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t qo = qo_indptr_h[i + 1] - qo_indptr_h[i];
+    const int64_t np = kv->indptr_h[i + 1] - kv->indptr_h[i];
+    const int64_t kvl = np > 0 ? (np - 1) * kv->page_size + kv->last_page_len_h[i] : 0;
+    for (int64_t qb = ceil_div(qo, p.q_per_wg) - 1; qb >= 0; --qb) {
+      const int64_t q_last = std::min<int64_t>((qb + 1) * p.q_per_wg, qo) - 1;
+      const int64_t key_end = p.causal ? std::min<int64_t>(kvl, q_last + (kvl - qo) + 1) : kvl;
+      items.emplace_back(key_end > 0 ? ceil_div(key_end, 64) : 0, (uint32_t)i << 16 | (uint32_t)qb);
+    }
+  }
+  std::stable_sort(items.begin(), items.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  for (size_t k = 0; k < items.size(); ++k) p.order[k] = items[k].second;
+  p.n_items = (int32_t)items.size();
+}
+
 fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
                                  const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
@@ -453,6 +482,7 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   p.v_scale = kv->v_scale;
   if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
                                        (long long)max_qo, 65535 * p.q_per_wg);
+  plan_prefill_order(p, batch, qo_indptr_h, kv);
   hipError_t err = fi::launch_prefill(p, q_dtype, kv->k_dtype, o_dtype, kv->head_dim, batch,
                                       reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));

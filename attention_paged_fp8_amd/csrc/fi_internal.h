@@ -70,6 +70,9 @@ struct MergeParams {
 
 // Prefill workgroups: waves of 32 query rows sharing each K/V tile.
 constexpr int kPrefillWaves = 8;
+// Largest number of (request, query block) pairs whose dispatch order travels
+// in the kernel arguments (4 bytes each).
+constexpr int kPrefillOrderMax = 768;
 
 struct PrefillParams {
   const void* q;          // [total_q, Hqo, D]
@@ -88,11 +91,16 @@ struct PrefillParams {
   int32_t num_kv_heads;
   int32_t group;
   int32_t heads_per_wg;   // 1, 2 or 4
-  int32_t q_per_wg;       // 128 / heads_per_wg query tokens per workgroup
-  int32_t n_qblocks;      // grid.y
+  int32_t q_per_wg;       // 32 * kPrefillWaves / heads_per_wg query tokens per workgroup
+  int32_t n_qblocks;      // grid.y when n_items == 0
   int32_t causal;
   float scale_log2;
   float v_scale;
+  // Dispatch order: when n_items > 0, workgroup x serves pair order[x / (kv
+  // heads * head groups)] = request << 16 | query block, listed heaviest
+  // first; otherwise x = (request, kv head, head group) and y = query block.
+  int32_t n_items;
+  uint32_t order[kPrefillOrderMax];
 };
 
 // Kernel launchers (defined in the .hip translation units).  They return the

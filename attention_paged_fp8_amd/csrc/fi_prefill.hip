@@ -112,8 +112,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   const int x = blockIdx.x;
   const int sg = x % nsg;
   const int g = (x / nsg) % p.num_kv_heads;
-  const int b = x / (nsg * p.num_kv_heads);
-  const int qb = p.n_qblocks - 1 - blockIdx.y;  // heaviest (latest) query blocks first
+  int b, qb;
+  if (p.n_items > 0) {  // (request, query block) pairs in the host's heaviest-first order
+    const uint32_t item = p.order[x / (nsg * p.num_kv_heads)];
+    b = (int)(item >> 16);
+    qb = (int)(item & 0xffffu);
+  } else {
+    b = x / (nsg * p.num_kv_heads);
+    qb = p.n_qblocks - 1 - blockIdx.y;  // latest query blocks first
+  }
 
   // request geometry: uniform over the workgroup, kept in scalar registers so
   // that the tile loop and its branches stay scalar
@@ -427,7 +434,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
 template <bool QBF16, int KVF, bool OBF16, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, int batch, hipStream_t s) {
   const int nsg = p.group / p.heads_per_wg;
-  dim3 grid(batch * p.num_kv_heads * nsg, p.n_qblocks);
+  const dim3 grid = (p.n_items > 0) ? dim3(p.n_items * p.num_kv_heads * nsg, 1)
+                                    : dim3(batch * p.num_kv_heads * nsg, p.n_qblocks);
   hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D>), grid, dim3(64 * kPrefillWaves), 0, s, p);
   return hipGetLastError();
 }
