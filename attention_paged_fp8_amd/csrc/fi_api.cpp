@@ -286,10 +286,7 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
     mp.part_o = p.part_o;
     mp.part_lse = p.part_lse;
     mp.nch = p.nch;
-    mp.indptr = p.indptr;
-    mp.last_page_len = p.last_page_len;
-    mp.page_size = p.page_size;
-    mp.single_kv_len = p.single_kv_len;
+    mp.batch = batch;
     mp.num_qo_heads = p.num_qo_heads;
     mp.group = p.group;
     mp.hpw_shift = p.hpw_shift;

@@ -393,6 +393,12 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
   }
   const int64_t T = pre[p.batch];
   const int64_t W = T * groups;
+  // requests without keys own no slice; their piece count 0 tells the merge
+  // kernel to write o = 0 and lse = -inf
+  if (p.nch)
+    for (int i = blockIdx.x; i < p.batch; i += gridDim.x)
+      if (pre[i + 1] == pre[i])
+        for (int k = tid; k < groups; k += 256) p.nch[(int64_t)i * groups + k] = 0;
   int64_t x0 = (int64_t)blockIdx.x * p.slice;
   const int64_t x1 = min(W, x0 + p.slice);
   while (x0 < x1) {
@@ -417,83 +423,75 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
 // ---------------------------------------------------------------------------
 // Split-KV merge: L = log2 sum_c 2^lse_c, o = v_scale * sum_c 2^(lse_c - L) o_c
 // (the natural-log form of the same identity is the oracle's merge_states).
-// One workgroup per (request, q head).  A (request, head) pair's partials are
-// contiguous over chunks, so the 256 threads stream them: thread t owns the
-// 4-float column quad t % (D/4) of every (256 / (D/4))-th chunk, and the
-// per-thread sums are reduced through LDS.
+// One wave per (request, q head), kMergeWaves per workgroup.  The segment's
+// piece count says what to do: 0 = a request without keys (o = 0, lse =
+// -inf), 1 = the decode kernel already wrote the result, n > 1 = merge n
+// partials.  Lane c holds chunk c's log-sum-exp (64 chunks per pass), the
+// lanes split head_dim, and the weights reach every lane through shuffles:
+// two dependent memory round trips (the count, then the partials), no LDS.
 // ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = 4;
 
 template <bool OBF16, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeParams p) {
-  constexpr int QUADS = D / 4;                      // float4 columns of a row
-  constexpr int LANES = kMergeThreads / QUADS;      // chunks processed side by side
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ f32x4_t part[LANES][QUADS];
-  const int hq = blockIdx.x % p.num_qo_heads;
-  const int b = blockIdx.x / p.num_qo_heads;
-  const int tid = threadIdx.x;
-  int kv_len;
-  if (p.indptr) {
-    const int a = p.indptr[b], e = p.indptr[b + 1];
-    kv_len = (e > a) ? (e - a - 1) * p.page_size + p.last_page_len[b] : 0;
-  } else {
-    kv_len = p.single_kv_len;
-  }
-  if (kv_len == 0) {  // a request without keys: o = 0, lse = -inf
-    if (tid < QUADS) {
-      uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + 4 * tid;
-      *reinterpret_cast<uint2*>(op) = make_uint2(0u, 0u);
-    }
-    if (p.lse && tid == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = kNegInf;
-    return;
-  }
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const MergeParams p) {
+  constexpr int PL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (pair >= p.batch * p.num_qo_heads) return;
+  const int hq = pair % p.num_qo_heads;
+  const int b = pair / p.num_qo_heads;
   // the (head group, slice group) this q head belongs to, as the decode kernel numbers them
   const int gkv = hq / p.group;
   const int sub = (hq - gkv * p.group) / kDecodeRows;
   const int grp = (sub / p.spw) * p.n_hgroups + (gkv >> p.hpw_shift);
-  const int nchunks = min(p.max_chunks, p.nch[(int64_t)b * p.n_hgroups * p.n_sgroups + grp]);
-  if (nchunks <= 1) return;
+  const int n = min(p.max_chunks, p.nch[(int64_t)b * p.n_hgroups * p.n_sgroups + grp]);
+  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + PL * lane;
+  float* lsep = p.lse ? p.lse + (int64_t)b * p.num_qo_heads + hq : nullptr;
+  if (n == 1) return;
+  if (n <= 0) {
+    if constexpr (PL == 2) *reinterpret_cast<uint32_t*>(op) = 0u;
+    else *op = 0;
+    if (lsep && lane == 0) *lsep = kNegInf;
+    return;
+  }
   const int64_t base = ((int64_t)b * p.num_qo_heads + hq) * p.max_chunks;
   const float* lse = p.part_lse + base;
-  // block max of the chunks' log-sum-exps
+  const float* po = p.part_o + base * D + PL * lane;
   float M = kNegInf;
-  for (int c = tid; c < nchunks; c += kMergeThreads) M = fmaxf(M, lse[c]);
+  for (int c0 = 0; c0 < n; c0 += 64)
+    if (c0 + lane < n) M = fmaxf(M, lse[c0 + lane]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  // weighted sums
-  const int q = tid % QUADS;
-  const int ln = tid / QUADS;
   float L = 0.f;
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f32x4_t* po = reinterpret_cast<const f32x4_t*>(p.part_o + base * D) + q;
-#pragma unroll 4
-  for (int c = ln; c < nchunks; c += LANES) {
-    const float lc = lse[c];
-    const float wgt = (lc == kNegInf) ? 0.f : fast_exp2(lc - M);
-    L += wgt;
-    acc += wgt * po[(int64_t)c * QUADS];
+  float acc[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const float lc = (c0 + lane < n) ? lse[c0 + lane] : kNegInf;
+    const float wl = (lc == kNegInf) ? 0.f : fast_exp2(lc - M);
+    L += wl;
+    const int cn = min(64, n - c0);
+    // blocks of 8 partials: all 8 loads in flight before the first is used
+    for (int k0 = 0; k0 < cn; k0 += 8) {
+      float v[8][PL];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) v[k][i] = (k0 + k < cn) ? po[(int64_t)(c0 + k0 + k) * D + i] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wk = __shfl(wl, k0 + k);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) acc[i] += wk * v[k][i];
+      }
+    }
   }
-  part[ln][q] = acc;
-  // L: every thread of a column quad saw a disjoint set of chunks; sum over them
-  float Ls = (q == 0) ? L : 0.f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o);
-  if ((tid & 63) == 0) red[tid >> 6] = Ls;
-  __syncthreads();
-  if (tid >= QUADS) return;
-  const float Lt = red[0] + red[1] + red[2] + red[3];
-  f32x4_t sum = part[0][q];
-#pragma unroll
-  for (int l = 1; l < LANES; ++l) sum += part[l][q];
-  const float f = (Lt > 0.f) ? p.v_scale / Lt : 0.f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + hq) * D + 4 * q;
-  *reinterpret_cast<uint2*>(op) = make_uint2(pack2<OBF16>(sum[0] * f, sum[1] * f), pack2<OBF16>(sum[2] * f, sum[3] * f));
-  if (p.lse && tid == 0) p.lse[(int64_t)b * p.num_qo_heads + hq] = (Lt > 0.f) ? (M + fast_log2(Lt)) * kLn2 : kNegInf;
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  const float f = (L > 0.f) ? p.v_scale / L : 0.f;
+  if constexpr (PL == 2) *reinterpret_cast<uint32_t*>(op) = pack2<OBF16>(acc[0] * f, acc[1] * f);
+  else *op = to_bits<OBF16>(acc[0] * f);
+  if (lsep && lane == 0) *lsep = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -598,8 +596,8 @@ hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt
 }
 
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {
-  dim3 grid((unsigned)p.num_qo_heads * batch);
-  dim3 block(kMergeThreads);
+  dim3 grid((unsigned)(((int64_t)p.num_qo_heads * batch + kMergeWaves - 1) / kMergeWaves));
+  dim3 block(64 * kMergeWaves);
   if (o_fmt == FMT_BF16) {
     if (head_dim == 128)
       hipLaunchKernelGGL((merge_kernel<true, 128>), grid, block, 0, s, p);

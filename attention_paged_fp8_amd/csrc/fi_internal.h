@@ -56,11 +56,8 @@ struct MergeParams {
   float* lse;
   const float* part_o;
   const float* part_lse;
-  const int32_t* nch;     // [batch, groups] pieces per segment
-  const int32_t* indptr;
-  const int32_t* last_page_len;
-  int32_t page_size;
-  int32_t single_kv_len;
+  const int32_t* nch;     // [batch, groups] pieces per segment (0: a request without keys)
+  int32_t batch;
   int32_t num_qo_heads;
   int32_t group;          // q heads per kv head
   int32_t hpw_shift, spw, n_hgroups, n_sgroups;
