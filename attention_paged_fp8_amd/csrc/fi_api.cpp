@@ -235,6 +235,16 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
       slice = std::max<int64_t>(slice, fi::kChunkQuantum);
       p.balanced = 1;
       p.slice = slice;
+      p.pre_n = 0;
+      if (batch <= fi::kDecodePrefixMax && total_kv < 0x7fffffff) {
+        int64_t run = 0;
+        for (int32_t i = 0; i < batch; ++i) {
+          p.pre[i] = (int32_t)run;
+          run += kv_of(i);
+        }
+        p.pre[batch] = (int32_t)run;
+        p.pre_n = batch + 1;
+      }
       p.n_wg = (int32_t)ceil_div(W, slice);
       p.max_chunks = (int32_t)(ceil_div(std::max<int64_t>(max_kv, 1), slice) + 1);
       p.chunk = 0;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
     const int hgrp = grp % p.n_hgroups;
     const int sgrp = grp / p.n_hgroups;
     const int pg_base = p.indptr ? p.indptr[b] : 0;
-    const int nsteps = (t_end > t_begin) ? (t_end - t_begin + kDecodeStep - 1) / kDecodeStep : 0;
+    const int nsteps = uniform((t_end > t_begin) ? (t_end - t_begin + kDecodeStep - 1) / kDecodeStep : 0);
 
     // this wave's (kv head, slice) and the workgroup's heads
     const int g0 = hgrp << p.hpw_shift;
@@ -296,21 +296,25 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
       __syncthreads();  // the previous stages and page ids are no longer read
       for (int i = tid; i < cnt; i += 256) pids_s[i] = p.indices ? p.indices[pg_base + pg_lo + i] : 0;
       __syncthreads();
-      const int n = ws1 - ws0;
+      const int n = uniform(ws1 - ws0);
       auto step_of = [&](int k) { return ws0 + min(k, n - 1); };
       Regs ra, rb;
       load_step(step_of(0), ra);
+      __builtin_amdgcn_sched_barrier(0);  // step 0's loads go out first, so waiting for them leaves step 1's in flight
       load_step(step_of(1), rb);
+      // Steps go in pairs and both halves always store and load (an odd
+      // count repeats the last step's data into an unread stage), so every
+      // path round the loop issues the same memory operations and the waits
+      // for a step's data stay two steps behind its loads.
       for (int k = 0; k < n; k += 2) {
         store_step(step_of(k), ra, smem);
         load_step(step_of(k + 2), ra);
         __syncthreads();
         if (wave_ok) compute(step_of(k), smem);
-        if (k + 1 >= n) break;
         store_step(step_of(k + 1), rb, smem + Cfg::STAGE);
         load_step(step_of(k + 3), rb);
         __syncthreads();
-        if (wave_ok) compute(step_of(k + 1), smem + Cfg::STAGE);
+        if (wave_ok && k + 1 < n) compute(step_of(k + 1), smem + Cfg::STAGE);
       }
     }
 
@@ -361,8 +365,8 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
   // workgroup, so every workgroup streams the same number of bytes.  A slice
   // may cover the end of one request and the start of the next; each such
   // piece is a chunk of its (request, group) segment.
-  int64_t* pre = reinterpret_cast<int64_t*>(smem + Cfg::PREFIX);  // [batch + 1] token prefix sums
-  {
+  int64_t* pre_lds = reinterpret_cast<int64_t*>(smem + Cfg::PREFIX);  // [batch + 1] token prefix sums
+  if (p.pre_n == 0) {
     const int B = p.batch;
     const int per = (B + 255) / 256;
     int64_t local = 0;
@@ -384,20 +388,23 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
     for (int k = 0; k < per; ++k) {
       const int i = tid * per + k;
       if (i < B) {
-        pre[i] = run;
+        pre_lds[i] = run;
         run += request_kv_len(p, i);
       }
     }
-    if (tid == 0) pre[B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tid == 0) pre_lds[B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  const int64_t T = pre[p.batch];
+  // every index below is uniform: with host prefix sums these are scalar
+  // loads from the kernel arguments
+  auto pre = [&](int i) -> int64_t { return p.pre_n ? (int64_t)p.pre[i] : pre_lds[i]; };
+  const int64_t T = pre(p.batch);
   const int64_t W = T * groups;
   // requests without keys own no slice; their piece count 0 tells the merge
   // kernel to write o = 0 and lse = -inf
   if (p.nch)
     for (int i = blockIdx.x; i < p.batch; i += gridDim.x)
-      if (pre[i + 1] == pre[i])
+      if (pre(i + 1) == pre(i))
         for (int k = tid; k < groups; k += 256) p.nch[(int64_t)i * groups + k] = 0;
   int64_t x0 = (int64_t)blockIdx.x * p.slice;
   const int64_t x1 = min(W, x0 + p.slice);
@@ -407,15 +414,15 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
     int lo = 0, hi = p.batch;  // largest b with pre[b] <= pos (then pos < pre[b + 1])
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= pos) lo = mid; else hi = mid;
+      if (pre(mid) <= pos) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int64_t seg0 = grp * T + pre[b];
-    const int64_t seg1 = grp * T + pre[b + 1];
+    const int64_t seg0 = grp * T + pre(b);
+    const int64_t seg1 = grp * T + pre(b + 1);
     const int64_t end = min(seg1, x1);
     const int64_t w_first = seg0 / p.slice;
     const int nchunks = (int)((seg1 - 1) / p.slice - w_first + 1);
-    process(b, grp, (int)(pos - pre[b]), (int)(end - seg0), (int)(blockIdx.x - w_first), nchunks);
+    process(b, grp, (int)(pos - pre(b)), (int)(end - seg0), (int)(blockIdx.x - w_first), nchunks);
     x0 = end;
   }
 }

@@ -16,6 +16,7 @@ constexpr int kChunkQuantum = 64;       // split-KV chunk granularity (tokens)
 constexpr int kDecodeRows = 16;         // q rows per decode MFMA tile (one GQA slice)
 constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kBalancedMaxBatch = 1024; // largest batch the balanced decode split handles
+constexpr int kDecodePrefixMax = 768;   // largest batch whose token prefix sums travel in the kernel arguments
 
 struct DecodeParams {
   const void* q;          // [tokens, Hqo, D]
@@ -49,6 +50,11 @@ struct DecodeParams {
   float v_scale;
   float* part_o;          // [batch, Hqo, max_chunks, D] fp32, normalised, unscaled by v_scale
   float* part_lse;        // [batch, Hqo, max_chunks] base-2 log-sum-exp
+  // balanced: token prefix sums of the requests, from the host's page table
+  // (pre[i] = tokens of requests < i, i <= batch) when they fit; else
+  // pre_n = 0 and every workgroup scans the device page table itself
+  int32_t pre_n;
+  int32_t pre[kDecodePrefixMax + 1];
 };
 
 struct MergeParams {
