@@ -70,12 +70,13 @@ struct PrefillCfg {
   static constexpr int PER = (CHUNKS + NT - 1) / NT;  // per thread (the last round may be partial)
   static constexpr int NS = D / 16;             // QK k-steps (MFMA k = 16)
   static constexpr int NDB = D / 32;            // PV head_dim blocks of 32
-  // Head-dimension order of the LDS tiles.  An fp8 lane holds 16 consecutive
-  // dimensions (16c .. 16c+15) and stores their widened halves 128 bytes
-  // apart, so the 8 lanes of a row write two contiguous 128-byte runs: tile
-  // position p holds dimension dim_of(p).  2-byte tiles keep the natural order.
+  // Head-dimension order of the LDS tiles: position p holds dimension
+  // dim_of(p), each run of 16 dimensions split into halves D/2 positions
+  // apart.  An fp8 lane holds 16 consecutive dimensions and stores their
+  // widened halves 128 bytes apart; a 2-byte lane holds 8 and stores them in
+  // one of the halves -- either way the lanes of a row write two contiguous
+  // runs, and both cache types produce the same tile for the same values.
   __host__ __device__ static constexpr int dim_of(int p) {
-    if (!kFp8) return p;
     return p < D / 2 ? 16 * (p / 8) + p % 8 : 16 * ((p - D / 2) / 8) + 8 + (p - D / 2) % 8;
   }
 };
@@ -216,18 +217,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
     for (int j = 0; j < Cfg::PER; ++j)
       if (ld_on(j)) f.v[j] = load16(vb + goff[j]);
   };
-  // widen into q's type and store rows into an LDS slot; fp8 dimensions
-  // 16c..16c+7 go to position 8c and 16c+8..16c+15 to D/2 + 8c
+  // store rows into an LDS slot in the dim_of order, fp8 widened to q's type
   auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch) {
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j) {
       if (!ld_on(j)) continue;
       uint8_t* d = slot + ld_row[j] * pitch;
-      if constexpr (Cfg::kFp8) {
+      if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
         *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].x, r[j].y);
         *reinterpret_cast<uint4*>(d + D + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].z, r[j].w);
-      } else {
-        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = r[j];
+      } else {  // dimensions 8c..8c+7 to position 8(c/2) (c even) or D/2 + 8(c/2) (c odd)
+        *reinterpret_cast<uint4*>(d + 16 * (ld_col[j] >> 1) + D * (ld_col[j] & 1)) = r[j];
       }
     }
   };

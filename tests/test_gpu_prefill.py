@@ -4,17 +4,21 @@ ABI, against the float64 oracle.
 Cases: the causal prefill configuration (3) at full size -- four requests
 compared element by element and sampled rows of every request; a matrix of
 small shapes (GQA groups 1, 2, 3, 4, 8; head_dim 64 and 128; page sizes 1 to
-64; fp8 and same-type 2-byte KV; causal and non-causal; ragged query and
-prefix lengths that leave partial tiles); rows with no visible key; decode
-equal to prefill with one query per request; run-to-run determinism.
+128; fp8 and same-type 2-byte KV; causal and non-causal; ragged query and
+prefix lengths that leave partial tiles); rows with no visible key; requests
+without queries or without keys; decode equal to prefill with one query per
+request; run-to-run determinism and page-permutation invariance (bitwise);
+fp8 equal to the same values stored in the 2-byte type (bitwise); constant V;
+a head-major pool through its strides.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle.attention as OA
+from oracle.fp8 import fp8_table
 from workloads import make_config, make_paged
-from gpu_util import assert_parity, run_decode, run_prefill, say, upload
+from gpu_util import T2, assert_parity, paged_kv, run_decode, run_prefill, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +32,8 @@ SMALL = [
     ("e5m2", "f16", "f16", 32, 128, 64, 8, (100, 65), (40, 1), True),         # group 8 (two head subgroups)
     ("f16", "f16", "f16", 16, 128, 32, 8, (77, 256), (3, 128), True),
     ("bf16", "bf16", "bf16", 8, 64, 4, 2, (150,), (200,), True),
+    ("e4m3", "bf16", "bf16", 128, 128, 32, 8, (70, 300), (400, 2), False),  # page 128, non-causal with prefix
+    ("e5m2", "f16", "f16", 128, 64, 16, 4, (129, 64), (0, 190), True),
 ]
 
 
@@ -90,3 +96,86 @@ def test_decode_equals_prefill_one_query(gpu_device):
     assert np.max(np.abs(od - op)) <= 2e-2 and np.max(np.abs(ld - lp)) <= 1e-3
     o_ref, l_ref = OA.batch_decode(w)
     assert_parity(op, lp, o_ref, l_ref, "bf16", "prefill at qo_len=1")
+
+
+# ------------------------------------------------------------------ invariants
+def _prefill_mid(seed=51, kvd="e4m3", q="f16", extra_pages=0):
+    return make_paged(seed, qo_lens=[300, 17, 64, 129], prefix_lens=[700, 0, 1000, 63], hq=32, hkv=8, d=128,
+                      page=16, q=q, kvd=kvd, extra_pages=extra_pages)
+
+
+def test_prefill_page_permutation_bitwise(gpu_device):
+    """Moving every page elsewhere in the pool (indices remapped) changes no bit."""
+    say("prefill page permutation")
+    w = _prefill_mid(extra_pages=20)
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_prefill(w, d, causal=True)
+    P = w["k_pool"].shape[0]
+    perm = np.random.default_rng(5).permutation(P)
+    inv = np.argsort(perm)
+    w2 = dict(w, k_pool=w["k_pool"][perm], v_pool=w["v_pool"][perm], indices=inv[w["indices"]].astype(np.int32))
+    o2, l2, _ = run_prefill(w2, upload(w2, gpu_device), causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert_parity(o1, l1, o_ref, l_ref, "f16", "prefill page permutation")
+
+
+@pytest.mark.parametrize("kvd,q", [("e4m3", "f16"), ("e5m2", "bf16")])
+def test_prefill_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
+    """fp8 K/V give bit-identical output to the same values stored widened in
+    q's 2-byte type (the tiles the kernel builds are the same)."""
+    say("prefill prewidened", kvd, q)
+    w = _prefill_mid(kvd=kvd, q=q)
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_prefill(w, d, causal=True)
+    tab = fp8_table(kvd)
+    kw = tab[w["k_pool"]].astype(np.float32)
+    vw = tab[w["v_pool"]].astype(np.float32)
+    k2 = torch.from_numpy(kw).to(T2[q]).to(gpu_device)
+    v2 = torch.from_numpy(vw).to(T2[q]).to(gpu_device)
+    kv, keep = paged_kv(w, d, k=k2, v=v2, kv_dtype=q)
+    o2, l2, _ = run_prefill(w, d, causal=True, kv=kv)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_prefill_constant_v(gpu_device):
+    """Every token carries the same V row: each output row is that row times
+    v_scale (up to the output rounding), causal mask or not."""
+    say("prefill constant V")
+    w = _prefill_mid()
+    row = w["v_pool"][w["indices"][0], 0].copy()
+    w["v_pool"][:] = row
+    d = upload(w, gpu_device)
+    target = fp8_table("e4m3")[row] * w["v_scale"]  # [H_kv, D]
+    exp = np.repeat(target, 32 // 8, axis=0)
+    for causal in (True, False):
+        o, l, _ = run_prefill(w, d, causal=causal)
+        np.testing.assert_allclose(o, np.broadcast_to(exp.astype(np.float16).astype(np.float64), o.shape),
+                                   rtol=2e-3, atol=1e-6)
+
+
+def test_prefill_head_major_pool_layout(gpu_device):
+    """A pool stored [num_pages, H_kv, page_size, D] passed through its strides."""
+    say("prefill HND layout")
+    w = _prefill_mid(q="bf16")
+    d = upload(w, gpu_device)
+    k_hnd = d["k"].permute(0, 2, 1, 3).contiguous()
+    v_hnd = d["v"].permute(0, 2, 1, 3).contiguous()
+    kv, keep = paged_kv(w, d, k=k_hnd.permute(0, 2, 1, 3), v=v_hnd.permute(0, 2, 1, 3))
+    o, l, _ = run_prefill(w, d, causal=True, kv=kv)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert_parity(o, l, o_ref, l_ref, "bf16", "prefill HND")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_requests_without_queries_or_keys(gpu_device, causal):
+    """Requests with qo_len 0 produce nothing; requests with kv_len 0 give o = 0
+    and lse = -inf for every row; the others are unaffected."""
+    say("prefill empty requests", causal)
+    w = make_paged(61, qo_lens=[0, 40, 13, 0, 7], kv_lens=[5, 0, 200, 0, 7], hq=8, hkv=2, d=64, page=16,
+                   q="bf16", kvd="e5m2")
+    d = upload(w, gpu_device)
+    o, l, _ = run_prefill(w, d, causal=causal)
+    assert np.all(o[0:40] == 0) and np.all(np.isneginf(l[0:40]))
+    o_ref, l_ref = OA.batch_prefill(w, causal=causal)
+    assert_parity(o, l, o_ref, l_ref, "bf16", "prefill empty requests")
