@@ -15,8 +15,12 @@ every valid K and V element once at 1 byte (fp8), q, o, lse and the page table
 
 The same JSON line carries the causal-prefill figure (16 requests, qo_len
 256..1024 plus a prefix of 0..2048, 32/8 heads, head_dim 128, e4m3 K/V, f16):
-MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head,
-and the float64 oracle timed on the host cores on a bounded sample.
+MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head;
+beside it the long-context split-KV decode (8 requests of 32k..128k tokens,
+64/8 heads, page 64, e5m2) and the batch-decode shapes with f16 q/o over f16,
+bf16 (mixed 2-byte) and e4m3 caches, a plain device copy's bandwidth for
+context, and the float64 oracle timed on the host cores on a bounded sample.
+Roofline figures use the median of the per-call HIP events.
 """
 from __future__ import annotations
 
@@ -116,14 +120,14 @@ def _time_calls(fn, n_copies, steps, warmup, stream):
     return wall_ms, ev
 
 
-def run_decode_bench(steps, warmup, copies):
+def run_decode_bench(steps, warmup, copies, cfg=2, kvd=None):
     import torch
 
     from attention_paged_fp8_amd import fi
     from workloads import make_config
 
     dev = torch.device("cuda:0")
-    w = make_config(2)
+    w = make_config(cfg, kvd=kvd)
     q, idx, kvs, keep = _upload(w, dev, copies)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
@@ -192,6 +196,39 @@ def measured_traffic(kind: str, workload: str):
         return None
 
 
+def copy_bandwidth(mb: int = 512, steps: int = 20) -> float:
+    """GB/s of a plain device-to-device copy of `mb` MiB (read + write bytes):
+    the practical streaming rate of this part, for context."""
+    import torch
+
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    _, ev = _time_calls(lambda i: dst.copy_(src), 1, steps, 3, stream)
+    return 2 * n / (float(np.median(ev)) * 1e-3) / 1e9
+
+
+def decode_extra(steps, warmup):
+    """Long-context split-KV decode and the three KV types of the mixed-dtype
+    decode workload: HIP-event medians and HBM rates (context beside the main
+    line; each is a separate decode workload)."""
+    out = {}
+    for key, cfg, kvd, copies in (("long_context", 4, None, 2), ("kv_f16", 5, "f16", 2), ("kv_bf16_mixed", 5, "bf16", 2),
+                                  ("kv_e4m3", 5, "e4m3", 4)):
+        w, wall_ms, ev = run_decode_bench(steps, warmup, copies, cfg=cfg, kvd=kvd)
+        nb = decode_bytes(w)
+        med = float(np.median(ev))
+        out[key] = {"workload": w["name"] + (f"_kv_{kvd}" if kvd else ""), "bytes_per_call": nb,
+                    "us_median": round(med * 1e3, 2), "gbs": round(nb / (med * 1e-3) / 1e9, 1),
+                    "frac": round(nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"# {key}: {nb / 1e6:.1f} MB, median {med * 1e3:.1f} us -> {out[key]['gbs']} GB/s", file=sys.stderr,
+              flush=True)
+        import torch
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_copy_calibration(mb: int, reps: int = 5):
     """A plain device-to-device copy of `mb` MiB, `reps` times: the reference
     the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -242,6 +279,8 @@ def main():
                     help="run one path only (for per-kernel counter passes)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-context and mixed-dtype decode workloads and the copy bandwidth")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this library and benchmark run on one GPU only; "
@@ -265,18 +304,19 @@ def main():
         w, wall_ms, ev = run_decode_bench(args.steps, args.warmup, args.copies)
     nbytes = decode_bytes(w)
     value = nbytes / (wall_ms * 1e-3) / 1e9
-    ev_ms = float(ev.mean())
+    ev_ms = float(np.median(ev))
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
-    print(f"# decode: {nbytes / 1e6:.1f} MB per call, wall {wall_ms * 1e3:.1f} us/step, events mean "
-          f"{ev_ms * 1e3:.1f} us (min {ev.min() * 1e3:.1f}, max {ev.max() * 1e3:.1f})", file=sys.stderr, flush=True)
+    print(f"# decode: {nbytes / 1e6:.1f} MB per call, wall {wall_ms * 1e3:.1f} us/step, events median "
+          f"{ev_ms * 1e3:.1f} us (mean {ev.mean() * 1e3:.1f}, min {ev.min() * 1e3:.1f}, max {ev.max() * 1e3:.1f})",
+          file=sys.stderr, flush=True)
 
     prefill = None
     if args.only in ("all", "prefill"):
         pw, p_wall, p_ev = run_prefill_bench(args.prefill_steps, 3)
         flops = prefill_flops(pw)
-        p_ms = float(p_ev.mean())
+        p_ms = float(np.median(p_ev))
         tflops = flops / (p_ms * 1e-3) / 1e12
-        print(f"# prefill: {flops / 1e9:.1f} GFLOP per call, events mean {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s",
+        print(f"# prefill: {flops / 1e9:.1f} GFLOP per call, events median {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
         prefill = {
             "workload": pw["name"], "tflops": round(tflops, 2), "ms": round(p_ms, 5),
@@ -285,6 +325,12 @@ def main():
                          "traffic": measured_traffic("prefill", pw["name"]), "flops_per_launch": flops},
             "dtype": "f16",
         }
+
+    extra, copy_gbs = None, None
+    if args.only == "all" and not args.no_extra:
+        extra = decode_extra(max(5, args.steps // 2), 3)
+        copy_gbs = round(copy_bandwidth(), 1)
+        print(f"# plain device copy: {copy_gbs} GB/s", file=sys.stderr, flush=True)
 
     cpu = None if (args.no_cpu or args.only == "prefill") else cpu_baseline(w, args.cpu_budget)
 
@@ -309,10 +355,12 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode", w["name"]),
-            "kernel": "decode_kernel + merge_kernel (one C-ABI call, timed with HIP events on its stream)",
+            "kernel": "decode_kernel + merge_kernel (one C-ABI call; median of HIP events on its stream)",
             "bytes_per_launch": nbytes,
         },
         "prefill": prefill,
+        "decode_other": extra,
+        "copy_gbs": copy_gbs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
