@@ -81,15 +81,15 @@ struct PrefillCfg {
   }
 };
 
-// Instruction order for the block that computes S(j+1) = K Q^T while the
-// probabilities of S(j) are formed, then accumulates P V: a few K reads
-// ahead, then each QK MFMA followed by a share of the exponential work and
-// one more LDS read (K, then the V reads of the PV phase), then each PV MFMA
-// with its two transposed reads.
-// (sched_group_barrier masks: 0x008 MFMA, 0x002 VALU, 0x400 transcendental,
-// 0x100 LDS read.)
-template <int NQK, int NPV>
-__device__ __forceinline__ void schedule_overlap() {
+// Instruction order of the two blocks of a step (sched_group_barrier masks:
+// 0x008 MFMA, 0x002 VALU, 0x400 transcendental, 0x100 LDS read, 0x200 LDS
+// write).  Block 1 computes S(j+1) = K Q^T while the probabilities of S(j)
+// are formed: a few K reads ahead, then each QK MFMA followed by a share of
+// the exponential work and one more LDS read.  Block 2 accumulates P V while
+// the row max of S(j+1) is taken and the next K tile is widened into LDS:
+// each PV MFMA with its two transposed reads and a share of that VALU work.
+template <int NQK>
+__device__ __forceinline__ void schedule_qk_exp() {
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int i = 0; i < NQK; ++i) {
@@ -97,11 +97,17 @@ __device__ __forceinline__ void schedule_overlap() {
     __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+}
+template <int NPV>
+__device__ __forceinline__ void schedule_pv_max() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
 }
 
 template <bool QBF16, int KVF, bool OBF16, int D>
@@ -266,10 +272,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       }
     }
   };
-  // mask (tiles that cross the diagonal or the end), row max, lazy rescale:
-  // the reference max moves only when some row's max grows by more than 8
-  // (log2), so exp2 stays below 2^8; returns the max the exponents subtract
-  auto softmax_head = [&](int tile, f32x16_t(&s)[2]) -> float {
+  // mask of the keys a row does not see (only tiles that cross the diagonal
+  // or the end of the sequence)
+  auto mask = [&](int tile, f32x16_t(&s)[2]) {
     const int kbase = tile * Cfg::TK;
     if (kbase + Cfg::TK > wave_full_end) {
 #pragma unroll
@@ -280,10 +285,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
           if (t >= row_key_end) s[sub][i] = kNegInf;
         }
     }
+  };
+  // row max in base-2 logit units (scale > 0 keeps the order)
+  auto row_max = [&](const f32x16_t(&s)[2]) -> float {
     float mx = fmaxf(s[0][0], s[0][1]);  // then three-operand maxima over pairs
 #pragma unroll
     for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(s[i >> 4][i & 15], s[i >> 4][(i & 15) + 1]));
-    mx = max_half_swap(mx) * p.scale_log2;  // base-2 logits (scale > 0 keeps the order)
+    return max_half_swap(mx) * p.scale_log2;
+  };
+  // lazy rescale: the reference max moves only when some row's max grows by
+  // more than 8 (log2), so exp2 stays below 2^8; returns the max the
+  // exponents subtract
+  auto rebase = [&](float mx) -> float {
     const bool grow = mx > m_run + 8.f;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = fmaxf(m_run, mx);
@@ -335,31 +348,43 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   };
 
   // ---- the tile pipeline ---------------------------------------------------
-  // Step j: store K(j+2) into the slot K(j) used and fetch K(j+4); mask and
-  // take the row max of S(j); issue S(j+1) = K(j+1) Q^T on the matrix cores
-  // while the same wave turns S(j) into probabilities; accumulate P(j) V(j);
-  // one barrier; store V(j+2) into the slot V(j) used and fetch V(j+4).
+  // Step j: issue S(j+1) = K(j+1) Q^T on the matrix cores while the same wave
+  // turns S(j) into probabilities; accumulate P(j) V(j) while it masks S(j+1),
+  // takes its row max and stores K(j+2) into the slot K(j) used; move the
+  // reference max for S(j+1) (after P(j) V(j), which a rescale applies to);
+  // fetch K(j+4); one barrier; store V(j+2) into the slot V(j) used and fetch
+  // V(j+4).
   // K and V each have two LDS slots; the barrier orders every slot's readers
   // before its next writer and every writer before its readers.  Two register
   // sets keep tiles in flight two steps ahead; page ids are fetched one step
   // before the data they address.
   auto step = [&](int j, f32x16_t(&sc)[2], f32x16_t(&sn)[2], Fetch& f, const uint32_t(&pcur)[Cfg::PER],
-                  uint32_t(&pnext)[Cfg::PER], uint8_t* k_this, const uint8_t* k_next, uint8_t* v_this) {
-    store_k(f, k_this);
+                  uint32_t(&pnext)[Cfg::PER], uint8_t* k_this, const uint8_t* k_next, uint8_t* v_this,
+                  float& m_use) {
     locate(tile_of(j + 4), pcur);
-    load_k(f);
-    load_pids(tile_of(j + 5), pnext);
     if (j < ntw) {
-      const float m_use = softmax_head(j, sc);
       uint4 pop[4];
       // S(j+1) even past this wave's last tile (the slot then holds a
       // clamped copy and the result goes unused): no branch splits the
-      // matrix-core work from the exponentials it overlaps
+      // matrix-core work from the VALU work it overlaps
       qk(k_next, sn);
       exp_pack(sc, m_use, pop);
+      // the probabilities are materialised here, beside the QK products,
+      // rather than sunk past the mask branch into the PV block (emits nothing)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pop[u].x), "v"(pop[u].y), "v"(pop[u].z), "v"(pop[u].w));
+      schedule_qk_exp<2 * Cfg::NS>();
+      mask(j + 1, sn);
       pv(v_this, pop);
-      schedule_overlap<2 * Cfg::NS, 4 * Cfg::NDB>();
+      const float mx = row_max(sn);
+      store_k(f, k_this);
+      schedule_pv_max<4 * Cfg::NDB>();
+      m_use = rebase(mx);  // after P(j) V(j): a rescale applies to it
+    } else {
+      store_k(f, k_this);
     }
+    load_k(f);
+    load_pids(tile_of(j + 5), pnext);
     __syncthreads();
     store_v(f, v_this);
     load_v(f);
@@ -401,14 +426,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       store_v(f1, V1);
     }
     __syncthreads();
-    if (ntw > 0) qk(K0, s0);
+    float m_use = 0.f;
+    if (ntw > 0) {
+      qk(K0, s0);
+      mask(0, s0);
+      m_use = rebase(row_max(s0));
+    }
     __syncthreads();  // every wave has read K(0) before step 0 overwrites its slot
     // Steps go in pairs (the register roles swap) and every step stores,
     // loads and waits whether or not this wave computes, so every path
     // round the loop issues the same memory operations.
     for (int j = 0; j < ntiles; j += 2) {
-      step(j, s0, s1, fa, pb, pa, K0, K1, V0);
-      step(j + 1, s1, s0, fb, pa, pb, K1, K0, V1);
+      step(j, s0, s1, fa, pb, pa, K0, K1, V0, m_use);
+      step(j + 1, s1, s0, fb, pa, pb, K1, K0, V1, m_use);
     }
   }
 
