@@ -228,7 +228,16 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   // workgroup slot of the device (the default whenever a workspace is given).
   p.balanced = 0;
   if (workspace && !forced && batch <= fi::kBalancedMaxBatch && total_kv > 0) {
-    const int slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
+    // Workgroups: the device's resident capacity (CUs x occupancy), except
+    // that short streams run better at 2 per CU -- fewer, longer slices split
+    // fewer requests and spread start-up over more bytes (measured: a slice
+    // under ~640 KB of K/V loses at 3 per CU, one over ~850 KB gains).
+    int slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
+    const int cus = fi::device_cus();
+    if (slots > 0 && cus > 0 && slots / cus > 2) {
+      const int64_t row_bytes = (int64_t)(1 << hpw_shift) * head_dim * elem_bytes(kv_dtype) * 2;  // K + V per item
+      if (ceil_div(total_kv * groups, slots) * row_bytes < (640 << 10)) slots = 2 * cus;
+    }
     if (slots > 0) {
       const int64_t W = total_kv * groups;
       int64_t slice = round_up(ceil_div(W, slots), fi::kDecodeStep);

@@ -579,6 +579,17 @@ static int occupancy_kv(int kv, int o, int d) {
   }
 }
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
   // cached per (device, instantiation): the values cannot change while the process runs
   static std::atomic<int> cache[64][2][5][2][2];

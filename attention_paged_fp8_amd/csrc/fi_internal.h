@@ -113,6 +113,7 @@ hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s);
 // Workgroups of the decode kernel for these types that fit on the current device at once.
 int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim);
+int device_cus();  // compute units of the current device (0 on error), cached
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                           hipStream_t s);
 hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int dst_fmt, void* out, hipStream_t s);
