@@ -320,6 +320,101 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   return FI_OK;
 }
 
+// Dispatch order of causal / full prefill: the (request, query block) pairs
+// sorted by the number of K/V tiles they walk, heaviest first, so that the
+// hardware's in-order dispatch approximates longest-processing-time
+// scheduling and no workgroup is launched for an empty query block.  Left
+// empty (grid order) when the pairs do not fit in the kernel arguments.
+void plan_prefill_order(fi::PrefillParams& p, int32_t batch, const int32_t* qo_indptr_h,
+                               const std::vector<int64_t>& kv_len) {
+  p.n_items = 0;
+  if (batch >= 65536) return;
+  int64_t pairs = 0;
+  for (int32_t i = 0; i < batch; ++i) pairs += ceil_div(qo_indptr_h[i + 1] - qo_indptr_h[i], p.q_per_wg);
+  if (pairs > fi::kPrefillOrderMax) return;
+  std::vector<std::pair<int64_t, uint32_t>> items;  // (tiles, request << 16 | block)
+  items.reserve((size_t)pairs);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t qo = qo_indptr_h[i + 1] - qo_indptr_h[i];
+    const int64_t kvl = kv_len[i];
+    for (int64_t qb = ceil_div(qo, p.q_per_wg) - 1; qb >= 0; --qb) {
+      const int64_t q_last = std::min<int64_t>((qb + 1) * p.q_per_wg, qo) - 1;
+      const int64_t key_end = p.causal ? std::min<int64_t>(kvl, q_last + (kvl - qo) + 1) : kvl;
+      items.emplace_back(key_end > 0 ? ceil_div(key_end, 64) : 0, (uint32_t)i << 16 | (uint32_t)qb);
+    }
+  }
+  std::stable_sort(items.begin(), items.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  for (size_t k = 0; k < items.size(); ++k) p.order[k] = items[k].second;
+  p.n_items = (int32_t)items.size();
+}
+
+// Query-side checks shared by the prefill calls (after the dtype and head
+// checks): the host query ranges, then q / o pointers.  *max_qo receives the
+// longest request's query count.
+fi_status check_queries(const char* fn, const void* q, void* o, int32_t batch, const int32_t* qo_indptr,
+                               const int32_t* qo_indptr_h, int64_t* max_qo) {
+  if (batch > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  int64_t mx = 0, total = 0;
+  if (batch > 0 && qo_indptr_h[0] < 0) return fail(FI_E_ARG, fn, "qo_indptr[0]=%d is negative", qo_indptr_h[0]);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t n = (int64_t)qo_indptr_h[i + 1] - qo_indptr_h[i];
+    if (n < 0) return fail(FI_E_ARG, fn, "qo_indptr is decreasing at request %d", i);
+    mx = n > mx ? n : mx;
+    total += n;
+  }
+  if (total > 0) {
+    if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
+    if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
+  }
+  *max_qo = mx;
+  return FI_OK;
+}
+
+// Common tail of the prefill calls: work-group shape, scales, dispatch order
+// and the launch.  p already holds the tensors and the K/V addressing.
+fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi_dtype kv_dtype,
+                             fi_dtype o_dtype, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t causal, int64_t max_qo, const int32_t* qo_indptr_h,
+                             const std::vector<int64_t>& kv_len, float sm_scale, float k_scale, float v_scale,
+                             bool ragged, hipStream_t stream) {
+  p.num_qo_heads = num_qo_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_qo_heads / num_kv_heads;
+  p.heads_per_wg = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
+  p.q_per_wg = 32 * fi::kPrefillWaves / p.heads_per_wg;
+  p.n_qblocks = (int32_t)ceil_div(max_qo, p.q_per_wg);
+  p.causal = causal ? 1 : 0;
+  const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = scale * k_scale * fi::kLog2eHost;
+  p.v_scale = v_scale;
+  if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
+                                       (long long)max_qo, 65535 * p.q_per_wg);
+  plan_prefill_order(p, batch, qo_indptr_h, kv_len);
+  hipError_t err = fi::launch_prefill(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, ragged, stream);
+  if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));
+  return FI_OK;
+}
+
+// Checks on contiguous K/V rows (ragged or single): strides, pointers and
+// alignment of two pools of `rows` rows.
+fi_status check_rows(const char* fn, const void* k, const void* v, fi_dtype kv_dtype, int64_t stride_token,
+                            int64_t stride_head, int64_t rows) {
+  const int eb = elem_bytes(kv_dtype);
+  if (stride_token <= 0 || stride_head <= 0)
+    return fail(FI_E_SHAPE, fn, "strides must be positive (token %lld, head %lld)", (long long)stride_token,
+                (long long)stride_head);
+  if (stride_token * eb >= (1ll << 32) || stride_head * eb >= (1ll << 32))
+    return fail(FI_E_SHAPE, fn, "K/V strides must be below 4 GiB");
+  if ((stride_token * eb) % 16 || (stride_head * eb) % 16)
+    return fail(FI_E_ARG, fn, "K/V strides must give 16-byte aligned rows (token %lld, head %lld elements of %d bytes)",
+                (long long)stride_token, (long long)stride_head, eb);
+  if (rows > 0) {
+    if (!k || !v) return fail(FI_E_ARG, fn, "k and v must not be NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(FI_E_ARG, fn, "k and v must be 16-byte aligned");
+  }
+  return FI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,34 +506,6 @@ fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const
                     workspace, workspace_bytes, sm_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
 }
 
-// Dispatch order of causal / full prefill: the (request, query block) pairs
-// sorted by the number of K/V tiles they walk, heaviest first, so that the
-// hardware's in-order dispatch approximates longest-processing-time
-// scheduling and no workgroup is launched for an empty query block.  Left
-// empty (grid order) when the pairs do not fit in the kernel arguments.
-static void plan_prefill_order(fi::PrefillParams& p, int32_t batch, const int32_t* qo_indptr_h, const fi_paged_kv* kv) {
-  p.n_items = 0;
-  if (batch >= 65536) return;
-  int64_t pairs = 0;
-  for (int32_t i = 0; i < batch; ++i) pairs += ceil_div(qo_indptr_h[i + 1] - qo_indptr_h[i], p.q_per_wg);
-  if (pairs > fi::kPrefillOrderMax) return;
-  std::vector<std::pair<int64_t, uint32_t>> items;  // (tiles, request << 16 | block)
-  items.reserve((size_t)pairs);
-  for (int32_t i = 0; i < batch; ++i) {
-    const int64_t qo = qo_indptr_h[i + 1] - qo_indptr_h[i];
-    const int64_t np = kv->indptr_h[i + 1] - kv->indptr_h[i];
-    const int64_t kvl = np > 0 ? (np - 1) * kv->page_size + kv->last_page_len_h[i] : 0;
-    for (int64_t qb = ceil_div(qo, p.q_per_wg) - 1; qb >= 0; --qb) {
-      const int64_t q_last = std::min<int64_t>((qb + 1) * p.q_per_wg, qo) - 1;
-      const int64_t key_end = p.causal ? std::min<int64_t>(kvl, q_last + (kvl - qo) + 1) : kvl;
-      items.emplace_back(key_end > 0 ? ceil_div(key_end, 64) : 0, (uint32_t)i << 16 | (uint32_t)qb);
-    }
-  }
-  std::stable_sort(items.begin(), items.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-  for (size_t k = 0; k < items.size(); ++k) p.order[k] = items[k].second;
-  p.n_items = (int32_t)items.size();
-}
-
 fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
                                  const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
@@ -451,25 +518,18 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   if (st != FI_OK) return st;
   if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is negative", batch);
   if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
-  if (batch > 0) {
-    if (!qo_indptr || !qo_indptr_h) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
-  }
+  if (batch > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
   if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
   int64_t max_kv = 0, total_kv = 0;
   if ((st = check_paged(fn, batch, kv, &max_kv, &total_kv)) != FI_OK) return st;
-  int64_t max_qo = 0, total_qo = 0;
-  if (batch > 0 && qo_indptr_h[0] < 0) return fail(FI_E_ARG, fn, "qo_indptr[0]=%d is negative", qo_indptr_h[0]);
-  for (int32_t i = 0; i < batch; ++i) {
-    const int64_t n = (int64_t)qo_indptr_h[i + 1] - qo_indptr_h[i];
-    if (n < 0) return fail(FI_E_ARG, fn, "qo_indptr is decreasing at request %d", i);
-    max_qo = n > max_qo ? n : max_qo;
-    total_qo += n;
-  }
-  if (total_qo > 0) {
-    if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
-    if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
-  }
+  int64_t max_qo = 0;
+  if ((st = check_queries(fn, q, o, batch, qo_indptr, qo_indptr_h, &max_qo)) != FI_OK) return st;
   if (batch == 0 || max_qo == 0) return FI_OK;
+  std::vector<int64_t> kv_len((size_t)batch);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t np = kv->indptr_h[i + 1] - kv->indptr_h[i];
+    kv_len[i] = np > 0 ? (np - 1) * kv->page_size + kv->last_page_len_h[i] : 0;
+  }
   const int eb = elem_bytes(kv->k_dtype);
   fi::PrefillParams p{};
   p.q = q;
@@ -486,24 +546,94 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   p.last_page_len = kv->last_page_len;
   p.page_shift = ilog2(kv->page_size);
   p.page_size = kv->page_size;
-  p.num_qo_heads = num_qo_heads;
-  p.num_kv_heads = kv->num_kv_heads;
-  p.group = num_qo_heads / kv->num_kv_heads;
-  p.heads_per_wg = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
-  p.q_per_wg = 32 * fi::kPrefillWaves / p.heads_per_wg;
-  p.n_qblocks = (int32_t)ceil_div(max_qo, p.q_per_wg);
-  p.causal = causal ? 1 : 0;
-  const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)kv->head_dim);
-  p.scale_log2 = scale * kv->k_scale * fi::kLog2eHost;
-  p.v_scale = kv->v_scale;
-  if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
-                                       (long long)max_qo, 65535 * p.q_per_wg);
-  plan_prefill_order(p, batch, qo_indptr_h, kv);
-  hipError_t err = fi::launch_prefill(p, q_dtype, kv->k_dtype, o_dtype, kv->head_dim, batch,
-                                      reinterpret_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));
-  return FI_OK;
+  return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
+                     causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale, kv->v_scale, false,
+                     reinterpret_cast<hipStream_t>(stream));
 }
+
+fi_status fi_batch_prefill_ragged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
+                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                  const fi_ragged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                  float sm_scale, void* stream) {
+  static const char* fn = "fi_batch_prefill_ragged";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, true);
+  if (st != FI_OK) return st;
+  if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is negative", batch);
+  if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
+  if (batch > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
+  if (kv->num_tokens < 0) return fail(FI_E_SHAPE, fn, "num_tokens=%d is negative", kv->num_tokens);
+  if ((st = check_rows(fn, kv->k, kv->v, kv->k_dtype, kv->stride_token, kv->stride_head,
+                       batch > 0 ? kv->num_tokens : 0)) != FI_OK)
+    return st;
+  if (batch > 0 && (!kv->indptr || !kv->indptr_h))
+    return fail(FI_E_ARG, fn, "indptr (device) and indptr_h (host copy) must not be NULL");
+  std::vector<int64_t> kv_len((size_t)batch);
+  if (batch > 0 && kv->indptr_h[0] < 0) return fail(FI_E_ARG, fn, "indptr[0]=%d is negative", kv->indptr_h[0]);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t a = kv->indptr_h[i], e = kv->indptr_h[i + 1];
+    if (e < a) return fail(FI_E_ARG, fn, "indptr is decreasing at request %d (%d > %d)", i, a, e);
+    if (e - a >= (1 << 30))
+      return fail(FI_E_SHAPE, fn, "request %d has %d tokens; at most 2^30 - 1 are supported", i, e - a);
+    kv_len[i] = e - a;
+  }
+  if (batch > 0 && kv->indptr_h[batch] > kv->num_tokens)
+    return fail(FI_E_ARG, fn, "indptr[%d]=%d exceeds num_tokens=%d", batch, kv->indptr_h[batch], kv->num_tokens);
+  int64_t max_qo = 0;
+  if ((st = check_queries(fn, q, o, batch, qo_indptr, qo_indptr_h, &max_qo)) != FI_OK) return st;
+  if (batch == 0 || max_qo == 0) return FI_OK;
+  const int eb = elem_bytes(kv->k_dtype);
+  fi::PrefillParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(kv->k);
+  p.v = reinterpret_cast<const uint8_t*>(kv->v);
+  p.st = kv->stride_token * eb;
+  p.sh = kv->stride_head * eb;
+  p.qo_indptr = qo_indptr;
+  p.indptr = kv->indptr;
+  return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
+                     causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale, kv->v_scale, true,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, const void* k, const void* v,
+                            fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t causal, float k_scale, float v_scale,
+                            void* o, fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
+  static const char* fn = "fi_single_prefill";
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, k_dtype, v_dtype, true);
+  if (st != FI_OK) return st;
+  if ((st = check_heads(fn, num_qo_heads, num_kv_heads, head_dim)) != FI_OK) return st;
+  if (qo_len < 0) return fail(FI_E_SHAPE, fn, "qo_len=%d is negative", qo_len);
+  if (kv_len < 0 || kv_len >= (1 << 30)) return fail(FI_E_SHAPE, fn, "kv_len=%d is outside [0, 2^30)", kv_len);
+  if ((st = check_scales(fn, k_scale, v_scale, sm_scale)) != FI_OK) return st;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if ((st = check_rows(fn, k, v, k_dtype, row, head_dim, kv_len)) != FI_OK) return st;
+  if (qo_len > 0) {
+    if (!q || !o) return fail(FI_E_ARG, fn, "q and o must not be NULL");
+    if (!aligned16(q) || !aligned16(o)) return fail(FI_E_ARG, fn, "q and o must be 16-byte aligned");
+  }
+  if (qo_len == 0) return FI_OK;
+  const int eb = elem_bytes(k_dtype);
+  fi::PrefillParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(k);
+  p.v = reinterpret_cast<const uint8_t*>(v);
+  p.st = row * eb;
+  p.sh = (int64_t)head_dim * eb;
+  p.single_qo_len = qo_len;
+  p.single_kv_len = kv_len;
+  const int32_t qo_indptr_h[2] = {0, qo_len};
+  const std::vector<int64_t> lens(1, kv_len);
+  return run_prefill(fn, p, q_dtype, k_dtype, o_dtype, 1, num_qo_heads, num_kv_heads, head_dim, causal, qo_len,
+                     qo_indptr_h, lens, sm_scale, k_scale, v_scale, true, reinterpret_cast<hipStream_t>(stream));
+}
+
 
 fi_status fi_fp8_widen(const uint8_t* codes, int64_t n, fi_dtype src, fi_dtype dst, void* out, void* stream) {
   static const char* fn = "fi_fp8_widen";

@@ -85,11 +85,13 @@ struct PrefillParams {
   const uint8_t* v;
   int64_t sp, st, sh;     // bytes
   const int32_t* qo_indptr;
-  const int32_t* indptr;
+  const int32_t* indptr;  // pages per request; token rows per request when ragged
   const int32_t* indices;
   const int32_t* last_page_len;
   int32_t page_shift;
   int32_t page_size;
+  int32_t single_qo_len;  // when qo_indptr (and indptr) are NULL: the one request's
+  int32_t single_kv_len;  // queries and keys (ragged K/V from row 0)
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;
@@ -114,8 +116,9 @@ hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch
 // Workgroups of the decode kernel for these types that fit on the current device at once.
 int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim);
 int device_cus();  // compute units of the current device (0 on error), cached
+// ragged: K/V rows addressed as indptr[b] + t (stride st) instead of a page table
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
-                          hipStream_t s);
+                          bool ragged, hipStream_t s);
 hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int dst_fmt, void* out, hipStream_t s);
 
 }  // namespace fi

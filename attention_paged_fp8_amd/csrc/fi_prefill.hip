@@ -110,7 +110,10 @@ __device__ __forceinline__ void schedule_pv_max() {
   __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
 }
 
-template <bool QBF16, int KVF, bool OBF16, int D>
+// RAGGED: K/V rows are contiguous per request -- token t of request b is row
+// indptr[b] + t of the pools (or row t when indptr is NULL) -- so the page
+// walk reduces to an addition and no index is loaded.
+template <bool QBF16, int KVF, bool OBF16, int D, bool RAGGED>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const PrefillParams p) {
   using Cfg = PrefillCfg<QBF16, KVF, OBF16, D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
@@ -131,12 +134,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
 
   // request geometry: uniform over the workgroup, kept in scalar registers so
   // that the tile loop and its branches stay scalar
-  const int q_begin = uniform(p.qo_indptr[b]);
-  const int qo_len = uniform(p.qo_indptr[b + 1]) - q_begin;
+  // (a single request passes its lengths in the arguments instead of indptrs)
+  const int q_begin = p.qo_indptr ? uniform(p.qo_indptr[b]) : 0;
+  const int qo_len = p.qo_indptr ? uniform(p.qo_indptr[b + 1]) - q_begin : p.single_qo_len;
   const int q0 = qb * p.q_per_wg;
   if (q0 >= qo_len) return;
-  const int a = uniform(p.indptr[b]), e = uniform(p.indptr[b + 1]);
-  const int kv_len = (e > a) ? (e - a - 1) * p.page_size + uniform(p.last_page_len[b]) : 0;
+  const int a = p.indptr ? uniform(p.indptr[b]) : 0;
+  int kv_len;
+  if (RAGGED) {
+    kv_len = p.indptr ? uniform(p.indptr[b + 1]) - a : p.single_kv_len;
+  } else {
+    const int e = uniform(p.indptr[b + 1]);
+    kv_len = (e > a) ? (e - a - 1) * p.page_size + uniform(p.last_page_len[b]) : 0;
+  }
   const int prefix = kv_len - qo_len;
 
   const int tid = threadIdx.x;
@@ -201,9 +211,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   auto load_pids = [&](int tile, uint32_t(&pid)[Cfg::PER]) {
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j)
-      if (ld_on(j)) pid[j] = (uint32_t)p.indices[a + (row_token(tile, j) >> p.page_shift)];
+      if (ld_on(j)) {
+        if (RAGGED)
+          pid[j] = (uint32_t)(a + row_token(tile, j));  // the row itself
+        else
+          pid[j] = (uint32_t)p.indices[a + (row_token(tile, j) >> p.page_shift)];
+      }
   };
   auto offset = [&](int tile, int j, uint32_t pid) -> uint64_t {
+    if (RAGGED) return (uint64_t)pid * (uint32_t)p.st + (uint32_t)(ld_col[j] * 16);
     const int t = row_token(tile, j);
     return (uint64_t)pid * (uint32_t)p.sp + (uint32_t)((t & (p.page_size - 1)) * (uint32_t)p.st) +
            (uint32_t)(ld_col[j] * 16);
@@ -462,40 +478,44 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
 }
 
 template <bool QBF16, int KVF, bool OBF16, int D>
-static hipError_t launch_prefill_t(const PrefillParams& p, int batch, hipStream_t s) {
+static hipError_t launch_prefill_t(const PrefillParams& p, int batch, bool ragged, hipStream_t s) {
   const int nsg = p.group / p.heads_per_wg;
   const dim3 grid = (p.n_items > 0) ? dim3(p.n_items * p.num_kv_heads * nsg, 1)
                                     : dim3(batch * p.num_kv_heads * nsg, p.n_qblocks);
-  hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  if (ragged)
+    hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
   return hipGetLastError();
 }
 
 template <bool QBF16, int KVF, bool OBF16>
-static hipError_t launch_prefill_d(const PrefillParams& p, int head_dim, int batch, hipStream_t s) {
-  if (head_dim == 128) return launch_prefill_t<QBF16, KVF, OBF16, 128>(p, batch, s);
-  return launch_prefill_t<QBF16, KVF, OBF16, 64>(p, batch, s);
+static hipError_t launch_prefill_d(const PrefillParams& p, int head_dim, int batch, bool ragged, hipStream_t s) {
+  if (head_dim == 128) return launch_prefill_t<QBF16, KVF, OBF16, 128>(p, batch, ragged, s);
+  return launch_prefill_t<QBF16, KVF, OBF16, 64>(p, batch, ragged, s);
 }
 
 template <bool QBF16, int KVF>
-static hipError_t launch_prefill_o(const PrefillParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {
-  if (o_fmt == FMT_BF16) return launch_prefill_d<QBF16, KVF, true>(p, head_dim, batch, s);
-  return launch_prefill_d<QBF16, KVF, false>(p, head_dim, batch, s);
+static hipError_t launch_prefill_o(const PrefillParams& p, int o_fmt, int head_dim, int batch, bool ragged,
+                                   hipStream_t s) {
+  if (o_fmt == FMT_BF16) return launch_prefill_d<QBF16, KVF, true>(p, head_dim, batch, ragged, s);
+  return launch_prefill_d<QBF16, KVF, false>(p, head_dim, batch, ragged, s);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
-                          hipStream_t s) {
+                          bool ragged, hipStream_t s) {
   // Prefill admits a 2-byte KV only when it equals q's type.
   if (q_fmt == FMT_BF16) {
     switch (kv_fmt) {
-      case FMT_BF16: return launch_prefill_o<true, FMT_BF16>(p, o_fmt, head_dim, batch, s);
-      case FMT_E4M3: return launch_prefill_o<true, FMT_E4M3>(p, o_fmt, head_dim, batch, s);
-      default: return launch_prefill_o<true, FMT_E5M2>(p, o_fmt, head_dim, batch, s);
+      case FMT_BF16: return launch_prefill_o<true, FMT_BF16>(p, o_fmt, head_dim, batch, ragged, s);
+      case FMT_E4M3: return launch_prefill_o<true, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+      default: return launch_prefill_o<true, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
     }
   }
   switch (kv_fmt) {
-    case FMT_F16: return launch_prefill_o<false, FMT_F16>(p, o_fmt, head_dim, batch, s);
-    case FMT_E4M3: return launch_prefill_o<false, FMT_E4M3>(p, o_fmt, head_dim, batch, s);
-    default: return launch_prefill_o<false, FMT_E5M2>(p, o_fmt, head_dim, batch, s);
+    case FMT_F16: return launch_prefill_o<false, FMT_F16>(p, o_fmt, head_dim, batch, ragged, s);
+    case FMT_E4M3: return launch_prefill_o<false, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+    default: return launch_prefill_o<false, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
   }
 }
 

@@ -35,7 +35,7 @@ STATUS = {0: "FI_OK", 1: "FI_E_DTYPE", 2: "FI_E_SHAPE", 3: "FI_E_ARG", 4: "FI_E_
 
 # every symbol include/fi.h declares
 EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_prefill_paged",
-           "fi_single_decode", "fi_fp8_widen")
+           "fi_batch_prefill_ragged", "fi_single_prefill", "fi_single_decode", "fi_fp8_widen")
 
 
 class FiError(Exception):
@@ -66,6 +66,17 @@ class PagedKV(ctypes.Structure):
     ]
 
 
+class RaggedKV(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_dtype", ctypes.c_int), ("v_dtype", ctypes.c_int),
+        ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64),
+        ("num_tokens", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("indptr", ctypes.c_void_p), ("indptr_h", ctypes.c_void_p),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -89,6 +100,12 @@ def lib() -> ctypes.CDLL:
     L.fi_batch_prefill_paged.restype = en
     L.fi_batch_prefill_paged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(PagedKV), i32, vp, en, vp, f32, vp,
                                          sz, vp]
+    L.fi_batch_prefill_ragged.restype = en
+    L.fi_batch_prefill_ragged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(RaggedKV), i32, vp, en, vp, f32,
+                                          vp]
+    L.fi_single_prefill.restype = en
+    L.fi_single_prefill.argtypes = [vp, en, i32, vp, vp, en, en, i32, i32, i32, i32, i32, f32, f32, vp, en, vp, f32,
+                                    vp]
     L.fi_single_decode.restype = en
     L.fi_single_decode.argtypes = [vp, en, vp, vp, en, en, i32, i32, i32, i32, f32, f32, vp, en, vp, f32, vp, sz, vp]
     L.fi_fp8_widen.restype = en
@@ -191,6 +208,54 @@ def fi_batch_prefill_paged(q, qo_indptr, kv: PagedKV, o, *, causal=True, q_dtype
         int(batch if batch is not None else qh.numel() - 1), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
         ctypes.byref(kv), 1 if causal else 0, _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse),
         float(sm_scale), _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def make_ragged_kv(k, v, indptr, *, k_scale=1.0, v_scale=1.0, kv_dtype=None, k_dtype=None, v_dtype=None,
+                   indptr_h=None):
+    """Describe a ragged K/V: k and v are [num_tokens, H_kv, head_dim] tensors
+    with a contiguous last dimension, request i owning rows indptr[i] ..
+    indptr[i+1]-1; raw fp8 may be passed as uint8 with kv_dtype naming the
+    format.  Returns (struct, keepalive)."""
+    if tuple(k.stride()) != tuple(v.stride()) or k.shape != v.shape:
+        raise FiValueError(2, "k and v must have the same shape and strides")
+    kd = k_dtype if k_dtype is not None else (kv_dtype if kv_dtype is not None else k.dtype)
+    vd = v_dtype if v_dtype is not None else (kv_dtype if kv_dtype is not None else v.dtype)
+    ih = _host_i32(indptr_h if indptr_h is not None else indptr)
+    s = RaggedKV()
+    s.k, s.v = _ptr(k), _ptr(v)
+    s.k_dtype, s.v_dtype = _dt(kd), _dt(vd)
+    s.stride_token, s.stride_head = k.stride(0), k.stride(1)
+    s.num_tokens, s.num_kv_heads, s.head_dim = int(k.shape[0]), int(k.shape[1]), int(k.shape[2])
+    s.indptr, s.indptr_h = _ptr(indptr), ih.data_ptr()
+    s.k_scale, s.v_scale = float(k_scale), float(v_scale)
+    return s, (ih,)
+
+
+def fi_batch_prefill_ragged(q, qo_indptr, kv: RaggedKV, o, *, causal=True, q_dtype=None, o_dtype=None, lse=None,
+                            sm_scale=0.0, qo_indptr_h=None, batch=None, num_qo_heads=None, stream=None):
+    """q and o [total_q, H_qo, D]; qo_indptr [batch+1] int32 (device)."""
+    qh = _host_i32(qo_indptr_h if qo_indptr_h is not None else qo_indptr)
+    st = lib().fi_batch_prefill_ragged(
+        _ptr(q), _dt(q_dtype if q_dtype is not None else q.dtype), _ptr(qo_indptr), qh.data_ptr(),
+        int(batch if batch is not None else qh.numel() - 1), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
+        ctypes.byref(kv), 1 if causal else 0, _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse),
+        float(sm_scale), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def fi_single_prefill(q, k, v, o, *, causal=True, k_scale=1.0, v_scale=1.0, q_dtype=None, kv_dtype=None,
+                      k_dtype=None, v_dtype=None, o_dtype=None, lse=None, sm_scale=0.0, stream=None):
+    """q and o [qo_len, H_qo, D]; k and v contiguous [kv_len, H_kv, D]."""
+    kd = k_dtype if k_dtype is not None else (kv_dtype if kv_dtype is not None else k.dtype)
+    vd = v_dtype if v_dtype is not None else (kv_dtype if kv_dtype is not None else v.dtype)
+    st = lib().fi_single_prefill(
+        _ptr(q), _dt(q_dtype if q_dtype is not None else q.dtype), int(q.shape[0]), _ptr(k), _ptr(v), _dt(kd), _dt(vd),
+        int(k.shape[0]), int(q.shape[1]), int(k.shape[1]), int(k.shape[2]), 1 if causal else 0, float(k_scale),
+        float(v_scale), _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale),
+        _stream(stream, q, o))
     check(st)
     return o
 

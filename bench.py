@@ -15,8 +15,9 @@ every valid K and V element once at 1 byte (fp8), q, o, lse and the page table
 
 The same JSON line carries the causal-prefill figure (16 requests, qo_len
 256..1024 plus a prefix of 0..2048, 32/8 heads, head_dim 128, e4m3 K/V, f16):
-MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head;
-beside it the long-context split-KV decode (8 requests of 32k..128k tokens,
+MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head,
+and the same workload with its K/V stored contiguously per request through
+the ragged call; beside them the long-context split-KV decode (8 requests of 32k..128k tokens,
 64/8 heads, page 64, e5m2) and the batch-decode shapes with f16 q/o over f16,
 bf16 (mixed 2-byte) and e4m3 caches, a plain device copy's bandwidth for
 context, and the float64 oracle timed on the host cores on a bounded sample.
@@ -142,22 +143,34 @@ def run_decode_bench(steps, warmup, copies, cfg=2, kvd=None):
     return w, wall_ms, ev
 
 
-def run_prefill_bench(steps, warmup):
+def run_prefill_bench(steps, warmup, ragged=False):
+    """The causal prefill workload through the paged call, or (ragged) the
+    same K/V values stored contiguously per request through the ragged call."""
     import torch
 
     from attention_paged_fp8_amd import fi
-    from workloads import make_config
+    from workloads import make_config, ragged_rows
 
     dev = torch.device("cuda:0")
     w = make_config(3)
-    q, idx, kvs, keep = _upload(w, dev, 1)
+    q, idx, kvs, keep = _upload(w, dev, 0 if ragged else 1)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if ragged:
+        kr, vr, indptr = ragged_rows(w)
+        k, v = torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev)
+        ind = torch.from_numpy(indptr).to(dev)
+        rkv, rkeep = fi.make_ragged_kv(k, v, ind, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=w["kv_dtype"],
+                                       indptr_h=indptr)
 
     def step(i):
-        fi.fi_batch_prefill_paged(q, idx["qo_indptr"], kvs[0], o, causal=True, lse=lse,
-                                  qo_indptr_h=w["qo_indptr"], stream=stream)
+        if ragged:
+            fi.fi_batch_prefill_ragged(q, idx["qo_indptr"], rkv, o, causal=True, lse=lse,
+                                       qo_indptr_h=w["qo_indptr"], stream=stream)
+        else:
+            fi.fi_batch_prefill_paged(q, idx["qo_indptr"], kvs[0], o, causal=True, lse=lse,
+                                      qo_indptr_h=w["qo_indptr"], stream=stream)
 
     wall_ms, ev = _time_calls(step, 1, steps, warmup, stream)
     return w, wall_ms, ev
@@ -325,6 +338,11 @@ def main():
                          "traffic": measured_traffic("prefill", pw["name"]), "flops_per_launch": flops},
             "dtype": "f16",
         }
+        if not args.no_extra:
+            _, _, r_ev = run_prefill_bench(args.prefill_steps, 3, ragged=True)
+            r_ms = float(np.median(r_ev))
+            prefill["ragged"] = {"ms": round(r_ms, 5), "tflops": round(flops / (r_ms * 1e-3) / 1e12, 2)}
+            print(f"# prefill, ragged K/V: events median {r_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     extra, copy_gbs = None, None
     if args.only == "all" and not args.no_extra:

@@ -164,6 +164,49 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
                                  const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
                                  float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* K/V held contiguously per request ("ragged"): request i owns rows
+ * indptr[i] .. indptr[i+1]-1 of each pool, row r of kv head g at element
+ * r * stride_token + g * stride_head.  The default layout is
+ * [num_tokens, num_kv_heads, head_dim].  Same dtype and scale rules as
+ * fi_paged_kv. */
+typedef struct fi_ragged_kv {
+  const void* k;                /* [dev] K rows */
+  const void* v;                /* [dev] V rows (same strides as k) */
+  fi_dtype k_dtype, v_dtype;    /* must be equal */
+  int64_t stride_token;         /* elements between consecutive rows */
+  int64_t stride_head;          /* elements between consecutive kv heads */
+  int32_t num_tokens;           /* rows in each pool; indptr[batch] <= num_tokens */
+  int32_t num_kv_heads;
+  int32_t head_dim;             /* 64 or 128 */
+  const int32_t* indptr;        /* [dev] [batch+1] row ranges per request */
+  const int32_t* indptr_h;      /* [host] copy of indptr */
+  float k_scale, v_scale;       /* per-tensor, finite and > 0; 1.0 = none */
+} fi_ragged_kv;
+
+/* Batched prefill over a ragged (non-paged) K/V: the batch-prefill run entry
+ * point without a page table ([C] Architecture / design notes: the ragged
+ * wrapper and the run entry points that share the k/v dtype check; Test plan:
+ * the fp8 equivalence across single, paged and ragged).  Arguments, layouts,
+ * refusals and results as fi_batch_prefill_paged, with request i's kv_len =
+ * indptr[i+1] - indptr[i] (0: o = 0 and lse = -inf).  The same kernel runs,
+ * addressing rows instead of pages, so a ragged call and a paged call over the
+ * same K/V values give identical bits. */
+fi_status fi_batch_prefill_ragged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
+                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                  const fi_ragged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                  float sm_scale, void* stream);
+
+/* Prefill of one request against a contiguous K/V ([C] Architecture / design
+ * notes: the single-prefill run entry point).  q and o are [dev]
+ * [qo_len, num_qo_heads, head_dim]; k and v are [dev] [kv_len, num_kv_heads,
+ * head_dim]; lse is [qo_len, num_qo_heads] float32 or NULL.  Dtype rules,
+ * causal mask and results as fi_batch_prefill_paged with one request; no
+ * device index array is needed (the lengths travel in the kernel arguments). */
+fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, const void* k, const void* v,
+                            fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t causal, float k_scale, float v_scale,
+                            void* o, fi_dtype o_dtype, float* lse, float sm_scale, void* stream);
+
 /* Decode of one query against a contiguous K/V ([C] Summary: the single-decode
  * entry point).  k and v are [dev] [kv_len, num_kv_heads, head_dim] with the
  * same dtype rules as fi_batch_decode_paged; q and o are

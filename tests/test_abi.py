@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 6, names
+    assert len(names) == 8, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -100,6 +100,35 @@ def _single(L, q="f16", k="e4m3", v=None, o="default", d=64, hq=4, hkv=2, kv_len
                               1.0, 1.0, None, fi.DTYPES[o], None, 0.0, None, 0, None)
 
 
+def _ragged(k_dtype="e4m3", v_dtype=None, *, hkv=2, d=64, lens=(5, 17), lead=0, ptrs=False, num_tokens=None):
+    """A ragged-KV struct over host arrays; device pointers NULL unless ptrs."""
+    indptr = np.concatenate([[lead], lead + np.cumsum(lens)]).astype(np.int32)
+    s = fi.RaggedKV()
+    fake = 0x10000 if ptrs else None
+    s.k = s.v = fake
+    s.k_dtype = fi.DTYPES[k_dtype]
+    s.v_dtype = fi.DTYPES[v_dtype or k_dtype]
+    s.stride_token, s.stride_head = hkv * d, d
+    s.num_tokens = int(indptr[-1]) if num_tokens is None else num_tokens
+    s.num_kv_heads, s.head_dim = hkv, d
+    s.indptr = fake
+    s.indptr_h = indptr.ctypes.data
+    s.k_scale = s.v_scale = 1.0
+    return s, (indptr,)
+
+
+def _prefill_ragged(L, kv, q="f16", o="default", hq=4, batch=2, qp=None, op=None, qo_dev=None):
+    qo = np.array([0, 3, 7], np.int32)
+    return L.fi_batch_prefill_ragged(qp, fi.DTYPES[q], qo_dev, qo.ctypes.data, batch, hq, ctypes.byref(kv), 1, op,
+                                     fi.DTYPES[o], None, 0.0, None)
+
+
+def _single_prefill(L, q="f16", k="e4m3", v=None, o="default", d=64, hq=4, hkv=2, qo_len=5, kv_len=8, qp=None,
+                    kp=None, op=None):
+    return L.fi_single_prefill(qp, fi.DTYPES[q], qo_len, kp, kp, fi.DTYPES[k], fi.DTYPES[v or k], kv_len, hq, hkv, d,
+                               1, 1.0, 1.0, op, fi.DTYPES[o], None, 0.0, None)
+
+
 def _err(L):
     return L.fi_last_error().decode()
 
@@ -130,6 +159,17 @@ DTYPE_REFUSALS = [
     ("single", dict(k="u8"), 1, "fi_single_decode: KV cache has dtype uint8"),
     ("single", dict(o="e4m3"), 1, "fi_single_decode: o has dtype float8_e4m3fn"),
     ("single", dict(q="e4m3"), 1, "fi_single_decode: q has dtype float8_e4m3fn"),
+    ("ragged", dict(q="f16", k="bf16"), 1,
+     "fi_batch_prefill_ragged: q has dtype float16 but the KV cache has dtype bfloat16; prefill needs a 2-byte KV"),
+    ("ragged", dict(k="e4m3", v="e5m2"), 1, "fi_batch_prefill_ragged: k has dtype float8_e4m3fn but v has dtype"),
+    ("ragged", dict(k="i8"), 1, "fi_batch_prefill_ragged: KV cache has dtype int8, which has no float interpretation"),
+    ("ragged", dict(q="e4m3"), 1, "fi_batch_prefill_ragged: q has dtype float8_e4m3fn; an fp8 query"),
+    ("ragged", dict(o="e5m2"), 1, "fi_batch_prefill_ragged: o has dtype float8_e5m2"),
+    ("single_prefill", dict(q="bf16", k="f16"), 1,
+     "fi_single_prefill: q has dtype bfloat16 but the KV cache has dtype float16"),
+    ("single_prefill", dict(k="f16", v="bf16"), 1, "fi_single_prefill: k has dtype float16 but v has dtype bfloat16"),
+    ("single_prefill", dict(k="e5m2fnuz"), 1, "fi_single_prefill: KV cache has dtype float8_e5m2fnuz"),
+    ("single_prefill", dict(o="e4m3"), 1, "fi_single_prefill: o has dtype float8_e4m3fn"),
 ]
 
 
@@ -142,6 +182,11 @@ def test_dtype_refusals(L, call, kw, status, frag):
     o = kw.get("o", "default")
     if call == "single":
         st = _single(L, q=q, k=k, v=v, o=o)
+    elif call == "single_prefill":
+        st = _single_prefill(L, q=q, k=k, v=v, o=o)
+    elif call == "ragged":
+        kv, keep = _ragged(k, v)
+        st = _prefill_ragged(L, kv, q=q, o=o)
     else:
         kv, keep = _kv(k, v)
         st = _decode(L, kv, q=q, o=o) if call == "decode" else _prefill(L, kv, q=q, o=o)
@@ -203,6 +248,39 @@ def test_argument_refusals(L):
     kv6, keep6 = _kv(ptrs=True)
     kv6.stride_token = 2 * 64 + 4  # fp8 rows no longer 16-byte aligned
     assert _decode(L, kv6, qp=0x10000, op=0x10000) == 3 and "16-byte aligned rows" in _err(L)
+
+
+@no_gpu
+def test_ragged_and_single_prefill_refusals(L):
+    fake = 0x10000
+    kv, keep = _ragged()
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "k and v must not be NULL" in _err(L)
+    kv, keep = _ragged(ptrs=True, num_tokens=20)  # indptr ends at 22
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "indptr[2]=22 exceeds num_tokens=20" in _err(L)
+    kv, keep = _ragged(ptrs=True, lens=(5, -2))
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "indptr is decreasing at request 1" in _err(L)
+    kv, keep = _ragged(ptrs=True)
+    kv.indptr = None
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "indptr (device)" in _err(L)
+    kv, keep = _ragged(ptrs=True)
+    assert _prefill_ragged(L, kv, qp=fake, op=fake) == 3 and "qo_indptr and qo_indptr_h" in _err(L)
+    kv, keep = _ragged(ptrs=True, d=96)
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 2 and "head_dim=96" in _err(L)
+    kv, keep = _ragged(ptrs=True)
+    kv.stride_token = 2 * 64 + 4
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "16-byte aligned rows" in _err(L)
+    kv, keep = _ragged(ptrs=True)
+    kv.k_scale = float("inf")
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 3 and "k_scale" in _err(L)
+    assert _single_prefill(L, qo_len=-1) == 2 and "qo_len=-1 is negative" in _err(L)
+    assert _single_prefill(L, kv_len=1 << 30) == 2 and "kv_len=1073741824" in _err(L)
+    assert _single_prefill(L, qp=fake, op=fake) == 3 and "k and v must not be NULL" in _err(L)
+    assert _single_prefill(L, qp=fake + 8, op=fake, kp=fake) == 3 and "16-byte aligned" in _err(L)
+    assert _single_prefill(L, hq=6, hkv=4) == 2 and "num_qo_heads=6 is not a multiple" in _err(L)
+    # nothing to compute: accepted without touching the device
+    assert _single_prefill(L, qo_len=0, kv_len=0) == 0
+    kv, keep = _ragged(ptrs=True)
+    assert L.fi_batch_prefill_ragged(None, 1, None, None, 0, 4, ctypes.byref(kv), 1, None, 0, None, 0.0, None) == 0
 
 
 @no_gpu

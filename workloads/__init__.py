@@ -70,7 +70,7 @@ def cast_bits(x: np.ndarray, dtype: str) -> np.ndarray:
 def _encode_pool(x: np.ndarray, dtype: str, valid: np.ndarray):
     """Encode a float32 pool [P, page, H, d]; valid is a [P, page] bool mask."""
     P = x.shape[0]
-    step = max(1, (1 << 25) // max(1, x[0].size))
+    step = max(1, (1 << 25) // max(1, int(np.prod(x.shape[1:]))))  # rows per block (an empty pool has none)
     xt = torch.from_numpy(x)
     vt = torch.from_numpy(valid)
     if dtype in FP8_MAX:
@@ -180,3 +180,31 @@ def make_config(cfg_id: int, kvd: str | None = None) -> dict:
     w["name"] = c["name"]
     w["kind"] = c["kind"]
     return w
+
+
+def ragged_rows(w: dict, lead: int = 0, tail: int = 0):
+    """The K/V of a paged workload laid out contiguously per request
+    ("ragged"): request i's tokens, in logical order, become rows indptr[i] ..
+    indptr[i+1]-1 of [rows, H_kv, d] arrays of the same stored elements.
+    ``lead`` poisoned rows precede the first request and ``tail`` follow the
+    last, so a read outside the requests' rows shows up as a non-finite output.
+
+    Returns (k_rows, v_rows, indptr int32 [B+1]).  Data movement only."""
+    kv_lens = np.asarray(w["kv_lens"], dtype=np.int64)
+    B = len(kv_lens)
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[0] = lead
+    indptr[1:] = lead + np.cumsum(kv_lens)
+    rows = int(indptr[-1]) + tail
+    out = []
+    for name in ("k_pool", "v_pool"):
+        pool = w[name]
+        r = np.full((rows,) + pool.shape[2:], NAN_BITS[w["kv_dtype"]], dtype=pool.dtype)
+        for i in range(B):
+            n = int(kv_lens[i])
+            if n == 0:
+                continue
+            pages = w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
+            r[indptr[i]:indptr[i + 1]] = pool[pages].reshape((-1,) + pool.shape[2:])[:n]
+        out.append(r)
+    return out[0], out[1], indptr
