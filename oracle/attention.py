@@ -14,6 +14,9 @@ What is computed, and where the pages state it:
   * fp8 K/V with per-tensor k_scale / v_scale: real K = stored value * k_scale,
     real V = stored value * v_scale (PR #368, Test plan, the k_scale/v_scale
     item; PR #2148, review comments on the v_scale multiply).
+  * An fp8 query carries a per-tensor q_scale: real q = stored value *
+    q_scale (PR #2148, review comments: q_scale folded into sm_scale for the
+    first product).
   * The output has q's shape with V's head_dim (PR #2148, Nitpick comments).
   * Causal prefill (PR #368, Benchmark results).  Where the pages are silent
     (mask alignment, default softmax scale, log base of the LSE, empty
@@ -154,12 +157,21 @@ def paged_kv_values(w: dict, i: int):
     return k, v
 
 
+def query_values(w: dict) -> np.ndarray:
+    """Real-valued queries [tokens, H_qo, d]: the stored elements times the
+    per-tensor q_scale of an fp8 query (1 for a 2-byte query).  The scale
+    multiplies q exactly as k_scale multiplies K ("Enable Hopper FA3 FP8
+    attention in decode.py", flashinfer PR #2148, review comments: q_scale
+    folded into sm_scale for the first product)."""
+    return decode_elements(w["q"], w["q_dtype"]) * float(w.get("q_scale", 1.0))
+
+
 def batch_attention(w: dict, *, causal: bool, sm_scale=None, requests=None):
     """Attention for every request of a workload dict (see workloads.gen).
     Decode is qo_len = 1 per request (qo_indptr = arange(B+1)).
 
     Returns o [tokens, H_qo, d] and lse [tokens, H_qo] in float64."""
-    q_all = decode_elements(w["q"], w["q_dtype"])
+    q_all = query_values(w)
     d = q_all.shape[-1]
     scale = _resolve_scale(sm_scale, d)
     qo_indptr = w["qo_indptr"]
@@ -193,7 +205,7 @@ def single_decode(q_raw, q_dtype, k_raw, v_raw, kv_dtype, k_scale, v_scale, sm_s
 def attention_rows(w: dict, token_ids, head_ids, *, causal: bool, sm_scale=None):
     """Outputs for a sample of (query token, q head) pairs, each computed on its
     own: for checks at sizes where the full oracle would take too long."""
-    q_all = decode_elements(w["q"], w["q_dtype"])
+    q_all = query_values(w)
     d = q_all.shape[-1]
     scale = _resolve_scale(sm_scale, d)
     qo_indptr = np.asarray(w["qo_indptr"])

@@ -15,7 +15,7 @@ Pins, and what fixes them independently of the oracle's own code:
     query, split-and-merge equals the unsplit result, GQA equals MHA with
     repeated kv heads, and scaling k_scale by c equals scaling sm_scale by c
     (the fold recorded in "fp8 KV cache in the in-tree prefill kernel",
-    Test plan, k_scale/v_scale item);
+    Test plan, k_scale/v_scale item); the same for q_scale of an fp8 query;
   * causal: with no prefix, query row 0 sees only key 0 and the last row sees
     every key.
 """
@@ -48,7 +48,7 @@ def _torch_decode(raw, dtype):
 def brute_force(w, causal, sm_scale=None):
     """Scalar-loop definition: page walk slot by slot, exp without a max
     shift (inputs are tiny and logits small), explicit sums."""
-    q = _torch_decode(w["q"], w["q_dtype"])
+    q = _torch_decode(w["q"], w["q_dtype"]) * w.get("q_scale", 1.0)
     hq, d = q.shape[1], q.shape[2]
     hkv = w["k_pool"].shape[2]
     grp = hq // hkv
@@ -214,6 +214,26 @@ def pin_kscale_fold(M):
     np.testing.assert_allclose(o3, c * o4, atol=1e-13)
 
 
+def pin_fp8_query(M):
+    """An fp8 query with its per-tensor q_scale: brute force on tiny inputs,
+    and scaling q_scale by c equals scaling sm_scale by c (the fold of
+    "Enable Hopper FA3 FP8 attention in decode.py", flashinfer PR #2148,
+    review comments on q_scale)."""
+    for seed, q, kvd in ((11, "e4m3", "e4m3"), (12, "e5m2", "e4m3"), (13, "e4m3", "e5m2")):
+        w = make_paged(seed, qo_lens=[1, 3, 5], prefix_lens=[0, 2, 6], hq=4, hkv=2, d=8, page=4, q=q, kvd=kvd, o="f16")
+        assert w["q_scale"] != 1.0
+        o, l = M.batch_prefill(w, causal=True)
+        ob, lb = brute_force(w, causal=True)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+    c = 2.5
+    w2 = dict(w); w2["q_scale"] = w["q_scale"] * c
+    o1, l1 = M.batch_prefill(w2, causal=True, sm_scale=0.3)
+    o2, l2 = M.batch_prefill(w, causal=True, sm_scale=0.3 * c)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
 def pin_causal_rows(M):
     rng = np.random.default_rng(14)
     q = rng.standard_normal((6, 2, 4)); k = rng.standard_normal((6, 1, 4)); v = rng.standard_normal((6, 1, 4))
@@ -250,7 +270,7 @@ def pin_empty_request(M):
 
 PINS = [pin_empty_request, pin_brute_force_decode, pin_brute_force_prefill, pin_closed_forms, pin_weights_sum_to_one,
         pin_page_permutation, pin_decode_equals_prefill_one_query, pin_split_merge,
-        pin_gqa_equals_repeated_mha, pin_kscale_fold, pin_causal_rows, pin_sampled_rows]
+        pin_gqa_equals_repeated_mha, pin_kscale_fold, pin_fp8_query, pin_causal_rows, pin_sampled_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -273,6 +293,8 @@ MUTATIONS = {
     "merge_unweighted": ("o = (coef[..., None] * o_parts).sum(axis=0)", "o = o_parts.mean(axis=0)"),
     "transposed_pv": ("og = (w.reshape(n_q * group, n_kv) @ vg)", "og = (w.reshape(n_q * group, n_kv) @ vg[::-1])"),
     "default_scale_wrong": ("return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    "q_scale_dropped": ('return decode_elements(w["q"], w["q_dtype"]) * float(w.get("q_scale", 1.0))',
+                        'return decode_elements(w["q"], w["q_dtype"])'),
 }
 
 

@@ -18,7 +18,8 @@ Draw order for one workload (numpy default_rng(seed)):
   2. the page order: ``arange`` when pages are contiguous, else a permutation of
      the page pool (the pool holds exactly the pages needed, plus
      ``extra_pages`` unreferenced ones);
-  3. q, standard normal float32, cast to q's dtype;
+  3. q, standard normal float32, cast to q's dtype (an fp8 query is scaled
+     per tensor like K and V below: q_scale = amax / max finite);
   4. K, then V: standard normal float32 over the whole pool.  fp8: per-tensor
      scale = amax over valid slots / max finite (448 for e4m3, 57344 for e5m2);
      x / scale clamped to +-max finite, cast round-to-nearest-even.  2-byte:
@@ -133,7 +134,11 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
     qo_indptr = np.zeros(B + 1, dtype=np.int32)
     qo_indptr[1:] = np.cumsum(qo_lens)
     q32 = rng.standard_normal((int(qo_indptr[-1]), hq, d), dtype=np.float32)
-    q_bits = cast_bits(q32, q)
+    if q in FP8_MAX:  # an fp8 query: per-tensor scale amax / max finite, as for K and V
+        q_bits, q_scale = _encode_pool(q32[:, None], q, np.ones((q32.shape[0], 1), dtype=bool))
+        q_bits = q_bits[:, 0]
+    else:
+        q_bits, q_scale = cast_bits(q32, q), 1.0
     del q32
 
     # valid-slot mask over the pool [P, page]
@@ -157,7 +162,7 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
         scales[name] = sc
 
     return dict(
-        seed=seed, q=q_bits, q_dtype=q, kv_dtype=kvd, o_dtype=o or q,
+        seed=seed, q=q_bits, q_dtype=q, q_scale=q_scale, kv_dtype=kvd, o_dtype=o or (q if q in ("f16", "bf16") else "f16"),
         k_pool=pools["k"], v_pool=pools["v"], k_scale=scales["k"], v_scale=scales["v"],
         indptr=indptr, indices=indices, last_page_len=last_page_len, page_size=page,
         qo_indptr=qo_indptr, kv_lens=kv_lens.astype(np.int64), qo_lens=qo_lens.astype(np.int64),
