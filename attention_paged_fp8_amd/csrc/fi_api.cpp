@@ -66,7 +66,8 @@ fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_d
   if (!is_2byte(q)) {
     if (is_any_fp8(q))
       return fail(FI_E_DTYPE, fn, "q has dtype %s; an fp8 query is not supported (q must be float16 or bfloat16, "
-                  "and it is never cast silently)", dtype_name(q));
+                  "and it is never cast silently; fi_batch_prefill_paged_fp8q takes an fp8 query with its scale)",
+                  dtype_name(q));
     return fail(FI_E_DTYPE, fn, "q has dtype %s; q must be float16 or bfloat16", dtype_name(q));
   }
   if (*o == FI_DTYPE_DEFAULT) *o = q;
@@ -87,6 +88,33 @@ fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_d
   if (prefill && is_2byte(k) && k != q)
     return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; prefill needs a 2-byte KV cache of the "
                 "query's dtype (fp8 KV is widened on load)", dtype_name(q), dtype_name(k));
+  return FI_OK;
+}
+
+// Checks 1-5 for a call that takes an fp8 query: q in {e4m3, e5m2}; o given
+// explicitly as a 2-byte type (the default, q's dtype, would be fp8); k == v;
+// an fp8 KV cache.
+fi_status check_dtypes_fp8q(const char* fn, fi_dtype q, fi_dtype o, fi_dtype k, fi_dtype v) {
+  if (!is_ocp_fp8(q))
+    return fail(FI_E_DTYPE, fn, "q has dtype %s; this call takes an fp8 query (float8_e4m3fn or float8_e5m2)",
+                dtype_name(q));
+  if (o == FI_DTYPE_DEFAULT)
+    return fail(FI_E_DTYPE, fn, "o_dtype must be given for an fp8 query (float16 or bfloat16; the query's own dtype "
+                "is fp8, and an fp8 output is not supported)");
+  if (is_any_fp8(o))
+    return fail(FI_E_DTYPE, fn, "o has dtype %s; an fp8 output is not supported (o must be float16 or bfloat16)",
+                dtype_name(o));
+  if (!is_2byte(o)) return fail(FI_E_DTYPE, fn, "o has dtype %s; o must be float16 or bfloat16", dtype_name(o));
+  if (k != v) return fail(FI_E_DTYPE, fn, "k has dtype %s but v has dtype %s", dtype_name(k), dtype_name(v));
+  if (k == FI_I8 || k == FI_U8)
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be "
+                "float8_e4m3fn or float8_e5m2", dtype_name(k));
+  if (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ)
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; this library decodes OCP "
+                "float8_e4m3fn / float8_e5m2", dtype_name(k));
+  if (!is_ocp_fp8(k))
+    return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; an fp8 query needs an fp8 KV cache "
+                "(float8_e4m3fn or float8_e5m2)", dtype_name(q), dtype_name(k));
   return FI_OK;
 }
 
@@ -548,6 +576,50 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   p.page_size = kv->page_size;
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale, kv->v_scale, false,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
+                                      const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                      const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                      float sm_scale, void* stream) {
+  static const char* fn = "fi_batch_prefill_paged_fp8q";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes_fp8q(fn, q_dtype, o_dtype, kv->k_dtype, kv->v_dtype);
+  if (st != FI_OK) return st;
+  if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is negative", batch);
+  if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
+  if (batch > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  if (!std::isfinite(q_scale) || !(q_scale > 0.f)) return fail(FI_E_ARG, fn, "q_scale=%g must be finite and > 0", q_scale);
+  if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
+  int64_t max_kv = 0, total_kv = 0;
+  if ((st = check_paged(fn, batch, kv, &max_kv, &total_kv)) != FI_OK) return st;
+  int64_t max_qo = 0;
+  if ((st = check_queries(fn, q, o, batch, qo_indptr, qo_indptr_h, &max_qo)) != FI_OK) return st;
+  if (batch == 0 || max_qo == 0) return FI_OK;
+  std::vector<int64_t> kv_len((size_t)batch);
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t np = kv->indptr_h[i + 1] - kv->indptr_h[i];
+    kv_len[i] = np > 0 ? (np - 1) * kv->page_size + kv->last_page_len_h[i] : 0;
+  }
+  fi::PrefillParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = reinterpret_cast<const uint8_t*>(kv->k);
+  p.v = reinterpret_cast<const uint8_t*>(kv->v);
+  p.sp = kv->stride_page;  // fp8: one byte per element
+  p.st = kv->stride_token;
+  p.sh = kv->stride_head;
+  p.qo_indptr = qo_indptr;
+  p.indptr = kv->indptr;
+  p.indices = kv->indices;
+  p.last_page_len = kv->last_page_len;
+  p.page_shift = ilog2(kv->page_size);
+  p.page_size = kv->page_size;
+  // q_scale joins k_scale in the logit scale (both multiply the fp32 products)
+  return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
+                     causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * q_scale, kv->v_scale, false,
                      reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -150,6 +150,22 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
   }
 }
 
+// fp8 x fp8 -> fp32, 32x32 outputs over k = 64 (v_mfma_f32_32x32x64_f8f6f4,
+// unscaled).  Each lane supplies 32 bytes of A (row lane % 32) and of B
+// (column lane % 32); A and B share the assignment of (lane / 32, byte) to k,
+// so any split of the 64 k positions works as long as both operands use it.
+// The output layout is that of the 16-bit 32x32 MFMAs.  FA / FB name the
+// operands' formats (FMT_E4M3 or FMT_E5M2).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int FA, int FB>
+__device__ __forceinline__ f32x16_t mfma32x32x64_f8(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x16_t c) {
+  const i32x8_t a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8_t b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA == FMT_E5M2 ? 1 : 0, FB == FMT_E5M2 ? 1 : 0, 0, 0,
+                                                         0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Scalars
 // ---------------------------------------------------------------------------

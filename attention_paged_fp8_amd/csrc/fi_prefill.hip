@@ -42,13 +42,18 @@
 // separate sum of the fp32 values.
 // Each wave also overlaps its two phases: the QK MFMAs of the next tile are
 // issued between the exponentials of the current one.
+#include <type_traits>
+
 #include "fi_device.hpp"
 
 namespace fi {
 
-template <bool QBF16, int KVF, bool OBF16, int D>
+// Q8: an fp8 query; K stays fp8 in LDS and S = K Q^T runs on the fp8 MFMA,
+// while P V runs in fp16 (QBF16 is then false).
+template <bool QBF16, int KVF, bool OBF16, int D, bool Q8>
 struct PrefillCfg {
   static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
+  static_assert(!Q8 || kFp8, "an fp8 query needs an fp8 KV cache");
   // The output is normalised by the sum of the probabilities as rounded for
   // the PV MFMA.  fp16 rounds at 2^-11 and that sum also gives the
   // log-sum-exp; bf16 rounds at 2^-9, so its log-sum-exp uses a separate sum
@@ -58,7 +63,10 @@ struct PrefillCfg {
   static constexpr int TK = 64;                 // keys per tile
   static constexpr int DB = D * KVB;            // stored bytes of a row
   static constexpr int ROW = D * 2;             // bytes of a 2-byte row
-  static constexpr int KP = ROW + 16;           // K tile pitch, 16 mod 256 bytes
+  // K tile pitch: 16 mod 256 bytes for 2-byte rows; raw fp8 rows (Q8) take
+  // D + 16, an odd multiple of 16 bytes, so the 16-byte reads of 16
+  // consecutive rows fall in distinct bank groups
+  static constexpr int KP = Q8 ? D + 16 : ROW + 16;
   static constexpr int VP = (ROW + 191) / 256 * 256 + 64;  // V tile pitch, 64 mod 256 bytes
   static constexpr int KTILE = TK * KP;
   static constexpr int VTILE = TK * VP;
@@ -69,6 +77,7 @@ struct PrefillCfg {
   static constexpr int CHUNKS = TK * DB / 16;       // 16-byte pieces of a tile of one tensor
   static constexpr int PER = (CHUNKS + NT - 1) / NT;  // per thread (the last round may be partial)
   static constexpr int NS = D / 16;             // QK k-steps (MFMA k = 16)
+  static constexpr int NS8 = D / 64;            // QK k-steps of the fp8 MFMA (k = 64)
   static constexpr int NDB = D / 32;            // PV head_dim blocks of 32
   // Head-dimension order of the LDS tiles: position p holds dimension
   // dim_of(p), each run of 16 dimensions split into halves D/2 positions
@@ -98,6 +107,19 @@ __device__ __forceinline__ void schedule_qk_exp() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
+// Block 1 with the fp8 QK MFMA (k = 64, twice the work of a 16-bit one):
+// each MFMA with its two 16-byte K reads and a larger share of the
+// exponential work.
+template <int NQK>
+__device__ __forceinline__ void schedule_qk8_exp() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 20, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
 template <int NPV>
 __device__ __forceinline__ void schedule_pv_max() {
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -113,9 +135,11 @@ __device__ __forceinline__ void schedule_pv_max() {
 // RAGGED: K/V rows are contiguous per request -- token t of request b is row
 // indptr[b] + t of the pools (or row t when indptr is NULL) -- so the page
 // walk reduces to an addition and no index is loaded.
-template <bool QBF16, int KVF, bool OBF16, int D, bool RAGGED>
+template <int QF, int KVF, bool OBF16, int D, bool RAGGED>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const PrefillParams p) {
-  using Cfg = PrefillCfg<QBF16, KVF, OBF16, D>;
+  constexpr bool QBF16 = QF == FMT_BF16;
+  constexpr bool Q8 = QF == FMT_E4M3 || QF == FMT_E5M2;
+  using Cfg = PrefillCfg<QBF16, KVF, OBF16, D, Q8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
   const int nsg = p.group / p.heads_per_wg;
@@ -174,8 +198,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
 
   // Q^T operand: lane (hh, rho) holds q[row rho] at the dimensions of K tile
   // positions (D/2)*hh + 8s + j, j = 0..7 (8 consecutive dimensions).
+  // fp8 query (Q8): for k-step c, lane (hh, rho) holds the 32 bytes of
+  // dimensions 64c + 32hh .. +31, in memory order (K rows are read the same way).
   uint4 qop[Cfg::NS];
-  {
+  if constexpr (Q8) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
+                        ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D + 32 * hh;
+#pragma unroll
+    for (int s = 0; s < 2 * Cfg::NS8; ++s)
+      qop[s] = row_ok ? *reinterpret_cast<const uint4*>(qp + 64 * (s >> 1) + 16 * (s & 1)) : make_uint4(0, 0, 0, 0);
+  } else {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
                          ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D;
 #pragma unroll
@@ -240,12 +272,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       if (ld_on(j)) f.v[j] = load16(vb + goff[j]);
   };
   // store rows into an LDS slot in the dim_of order, fp8 widened to q's type
-  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch) {
+  // (raw: fp8 K rows for the fp8 MFMA, as loaded)
+  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw) {
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j) {
       if (!ld_on(j)) continue;
       uint8_t* d = slot + ld_row[j] * pitch;
-      if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
+      if constexpr (decltype(raw)::value) {
+        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = r[j];
+      } else if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
         *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].x, r[j].y);
         *reinterpret_cast<uint4*>(d + D + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].z, r[j].w);
       } else {  // dimensions 8c..8c+7 to position 8(c/2) (c even) or D/2 + 8(c/2) (c odd)
@@ -253,8 +288,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       }
     }
   };
-  auto store_k = [&](const Fetch& f, uint8_t* slot) { store_rows(f.k, slot, Cfg::KP); };
-  auto store_v = [&](const Fetch& f, uint8_t* slot) { store_rows(f.v, slot, Cfg::VP); };
+  auto store_k = [&](const Fetch& f, uint8_t* slot) { store_rows(f.k, slot, Cfg::KP, std::integral_constant<bool, Q8>{}); };
+  auto store_v = [&](const Fetch& f, uint8_t* slot) { store_rows(f.v, slot, Cfg::VP, std::false_type{}); };
 
   // ---- per-wave attention state --------------------------------------------
   float m_run = kNegInf;  // running max (base-2 scaled logits), updated lazily
@@ -270,7 +305,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   // K: lane (hh, rho) reads row 32*sub + rho, bytes [D*hh + 16*st, +16).
   // V^T transposed reads: within each 16-lane group (same hh, same rho / 16),
   // lanes 4r..4r+3 name the four 8-byte pieces of row r of a 16-column block.
-  const int k_base = rho * Cfg::KP + D * hh;
+  const int k_base = rho * Cfg::KP + (Q8 ? 32 : D) * hh;
   const int v_base = (4 * hh + ((rho & 15) >> 2)) * Cfg::VP + 32 * (rho >> 4) + 8 * (rho & 3);
 
   // S^T = K Q^T for one tile, two 32-token halves; lane (hh, rho) then holds
@@ -281,10 +316,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[sub][j] = 0.f;
+      if constexpr (Q8) {
 #pragma unroll
-      for (int st = 0; st < Cfg::NS; ++st) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(kl + 32 * sub * Cfg::KP + 16 * st);
-        s[sub] = mfma32x32x16<QBF16>(kop, qop[st], s[sub]);
+        for (int c = 0; c < Cfg::NS8; ++c) {
+          const uint8_t* a = kl + 32 * sub * Cfg::KP + 64 * c;
+          s[sub] = mfma32x32x64_f8<KVF, QF>(*reinterpret_cast<const uint4*>(a), *reinterpret_cast<const uint4*>(a + 16),
+                                            qop[2 * c], qop[2 * c + 1], s[sub]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < Cfg::NS; ++st) {
+          const uint4 kop = *reinterpret_cast<const uint4*>(kl + 32 * sub * Cfg::KP + 16 * st);
+          s[sub] = mfma32x32x16<QBF16>(kop, qop[st], s[sub]);
+        }
       }
     }
   };
@@ -389,7 +433,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       // rather than sunk past the mask branch into the PV block (emits nothing)
 #pragma unroll
       for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pop[u].x), "v"(pop[u].y), "v"(pop[u].z), "v"(pop[u].w));
-      schedule_qk_exp<2 * Cfg::NS>();
+      if constexpr (Q8)
+        schedule_qk8_exp<2 * Cfg::NS8>();
+      else
+        schedule_qk_exp<2 * Cfg::NS>();
       mask(j + 1, sn);
       pv(v_this, pop);
       const float mx = row_max(sn);
@@ -477,45 +524,56 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
         (l_run > 0.f) ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
 }
 
-template <bool QBF16, int KVF, bool OBF16, int D>
+template <int QF, int KVF, bool OBF16, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, int batch, bool ragged, hipStream_t s) {
   const int nsg = p.group / p.heads_per_wg;
   const dim3 grid = (p.n_items > 0) ? dim3(p.n_items * p.num_kv_heads * nsg, 1)
                                     : dim3(batch * p.num_kv_heads * nsg, p.n_qblocks);
-  if (ragged)
-    hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<QBF16, KVF, OBF16, D, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  if (ragged) {
+    if constexpr (QF == FMT_E4M3 || QF == FMT_E5M2) return hipErrorInvalidValue;  // fp8 queries: paged calls only
+    else hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  } else
+    hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool QBF16, int KVF, bool OBF16>
+template <int QF, int KVF, bool OBF16>
 static hipError_t launch_prefill_d(const PrefillParams& p, int head_dim, int batch, bool ragged, hipStream_t s) {
-  if (head_dim == 128) return launch_prefill_t<QBF16, KVF, OBF16, 128>(p, batch, ragged, s);
-  return launch_prefill_t<QBF16, KVF, OBF16, 64>(p, batch, ragged, s);
+  if (head_dim == 128) return launch_prefill_t<QF, KVF, OBF16, 128>(p, batch, ragged, s);
+  return launch_prefill_t<QF, KVF, OBF16, 64>(p, batch, ragged, s);
 }
 
-template <bool QBF16, int KVF>
+template <int QF, int KVF>
 static hipError_t launch_prefill_o(const PrefillParams& p, int o_fmt, int head_dim, int batch, bool ragged,
                                    hipStream_t s) {
-  if (o_fmt == FMT_BF16) return launch_prefill_d<QBF16, KVF, true>(p, head_dim, batch, ragged, s);
-  return launch_prefill_d<QBF16, KVF, false>(p, head_dim, batch, ragged, s);
+  if (o_fmt == FMT_BF16) return launch_prefill_d<QF, KVF, true>(p, head_dim, batch, ragged, s);
+  return launch_prefill_d<QF, KVF, false>(p, head_dim, batch, ragged, s);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                           bool ragged, hipStream_t s) {
-  // Prefill admits a 2-byte KV only when it equals q's type.
+  // Prefill admits a 2-byte KV only when it equals q's type, and an fp8
+  // query only with an fp8 KV.
+  if (q_fmt == FMT_E4M3 || q_fmt == FMT_E5M2) {
+    if (kv_fmt != FMT_E4M3 && kv_fmt != FMT_E5M2) return hipErrorInvalidValue;
+    if (q_fmt == FMT_E4M3) {
+      if (kv_fmt == FMT_E4M3) return launch_prefill_o<FMT_E4M3, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+      return launch_prefill_o<FMT_E4M3, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
+    }
+    if (kv_fmt == FMT_E4M3) return launch_prefill_o<FMT_E5M2, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+    return launch_prefill_o<FMT_E5M2, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
+  }
   if (q_fmt == FMT_BF16) {
     switch (kv_fmt) {
-      case FMT_BF16: return launch_prefill_o<true, FMT_BF16>(p, o_fmt, head_dim, batch, ragged, s);
-      case FMT_E4M3: return launch_prefill_o<true, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
-      default: return launch_prefill_o<true, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
+      case FMT_BF16: return launch_prefill_o<FMT_BF16, FMT_BF16>(p, o_fmt, head_dim, batch, ragged, s);
+      case FMT_E4M3: return launch_prefill_o<FMT_BF16, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+      default: return launch_prefill_o<FMT_BF16, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
     }
   }
   switch (kv_fmt) {
-    case FMT_F16: return launch_prefill_o<false, FMT_F16>(p, o_fmt, head_dim, batch, ragged, s);
-    case FMT_E4M3: return launch_prefill_o<false, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
-    default: return launch_prefill_o<false, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
+    case FMT_F16: return launch_prefill_o<FMT_F16, FMT_F16>(p, o_fmt, head_dim, batch, ragged, s);
+    case FMT_E4M3: return launch_prefill_o<FMT_F16, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+    default: return launch_prefill_o<FMT_F16, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
   }
 }
 

@@ -85,7 +85,10 @@ def _upload(w, dev, copies: int):
             t = t.view(torch.int16).view(t2[w["kv_dtype"]])
         return t.to(dev)
 
-    q = torch.from_numpy(w["q"].view(np.int16)).view(t2[w["q_dtype"]]).to(dev)
+    if w["q_dtype"] in t2:
+        q = torch.from_numpy(w["q"].view(np.int16)).view(t2[w["q_dtype"]]).to(dev)
+    else:  # fp8 query codes
+        q = torch.from_numpy(np.ascontiguousarray(w["q"])).to(dev)
     idx = {n: torch.from_numpy(np.ascontiguousarray(w[n], dtype=np.int32)).to(dev)
            for n in ("indptr", "indices", "last_page_len", "qo_indptr")}
     kvs, keep = [], []
@@ -143,18 +146,19 @@ def run_decode_bench(steps, warmup, copies, cfg=2, kvd=None):
     return w, wall_ms, ev
 
 
-def run_prefill_bench(steps, warmup, ragged=False):
+def run_prefill_bench(steps, warmup, ragged=False, fp8q=False):
     """The causal prefill workload through the paged call, or (ragged) the
-    same K/V values stored contiguously per request through the ragged call."""
+    same K/V values stored contiguously per request through the ragged call,
+    or (fp8q) with its query quantised to e4m3 through the fp8-query call."""
     import torch
 
     from attention_paged_fp8_amd import fi
     from workloads import make_config, ragged_rows
 
     dev = torch.device("cuda:0")
-    w = make_config(3)
+    w = make_config(3, q="e4m3" if fp8q else None)
     q, idx, kvs, keep = _upload(w, dev, 0 if ragged else 1)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.float16, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     if ragged:
@@ -165,7 +169,11 @@ def run_prefill_bench(steps, warmup, ragged=False):
                                        indptr_h=indptr)
 
     def step(i):
-        if ragged:
+        if fp8q:
+            fi.fi_batch_prefill_paged_fp8q(q, idx["qo_indptr"], kvs[0], o, q_dtype="e4m3", q_scale=w["q_scale"],
+                                           o_dtype=w["o_dtype"], causal=True, lse=lse, qo_indptr_h=w["qo_indptr"],
+                                           stream=stream)
+        elif ragged:
             fi.fi_batch_prefill_ragged(q, idx["qo_indptr"], rkv, o, causal=True, lse=lse,
                                        qo_indptr_h=w["qo_indptr"], stream=stream)
         else:
@@ -343,6 +351,12 @@ def main():
             r_ms = float(np.median(r_ev))
             prefill["ragged"] = {"ms": round(r_ms, 5), "tflops": round(flops / (r_ms * 1e-3) / 1e12, 2)}
             print(f"# prefill, ragged K/V: events median {r_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+            _, _, f_ev = run_prefill_bench(args.prefill_steps, 3, fp8q=True)
+            f_ms = float(np.median(f_ev))
+            prefill["fp8_query"] = {"ms": round(f_ms, 5), "tflops": round(flops / (f_ms * 1e-3) / 1e12, 2),
+                                    "note": "QK on the fp8 MFMA, PV in f16"}
+            print(f"# prefill, fp8 query: events median {f_ms * 1e3:.1f} us -> {flops / (f_ms * 1e-3) / 1e12:.1f} "
+                  "TFLOP/s", file=sys.stderr, flush=True)
 
     extra, copy_gbs = None, None
     if args.only == "all" and not args.no_extra:

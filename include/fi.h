@@ -164,6 +164,28 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
                                  const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
                                  float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Batched prefill over the paged cache with an fp8 query ([A] review
+ * comments: q_scale folded into sm_scale for the first product; [A]
+ * Walkthrough and review comments: an fp8 input gives a float16 or bfloat16
+ * output, never fp8).
+ *   q        [dev] [qo_indptr[batch], num_qo_heads, head_dim] fp8 codes,
+ *            q_dtype in {FI_F8_E4M3, FI_F8_E5M2}; real q = code * q_scale
+ *   q_scale  per-tensor, finite and > 0
+ *   kv       the paged cache; KV dtype in {E4M3, E5M2} (either, with either
+ *            query format)
+ *   o_dtype  FI_F16 or FI_BF16, given explicitly (FI_DTYPE_DEFAULT, the
+ *            query's own dtype, is refused)
+ * Other arguments, layouts, the causal mask and results as
+ * fi_batch_prefill_paged.  S = Q K^T runs on the fp8 matrix cores with K
+ * staying fp8 from HBM to the MFMA; the products are exact and summed in
+ * fp32 as in the 2-byte path; P V runs in float16 (P rounded to float16, V
+ * widened exactly), so the result matches the 2-byte path to the same
+ * tolerance. */
+fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
+                                      const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                      const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                      float sm_scale, void* stream);
+
 /* K/V held contiguously per request ("ragged"): request i owns rows
  * indptr[i] .. indptr[i+1]-1 of each pool, row r of kv head g at element
  * r * stride_token + g * stride_head.  The default layout is

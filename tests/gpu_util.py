@@ -38,7 +38,7 @@ def dev_pool(pool: np.ndarray, kvd: str, device) -> torch.Tensor:
 
 def upload(w: dict, device) -> dict:
     d = dict(
-        q=dev_2byte(w["q"], w["q_dtype"], device),
+        q=dev_pool(w["q"], w["q_dtype"], device),  # fp8 queries stay raw codes
         k=dev_pool(w["k_pool"], w["kv_dtype"], device),
         v=dev_pool(w["v_pool"], w["kv_dtype"], device),
         indptr=torch.from_numpy(w["indptr"]).to(device),

@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -129,6 +129,12 @@ def _single_prefill(L, q="f16", k="e4m3", v=None, o="default", d=64, hq=4, hkv=2
                                1, 1.0, 1.0, op, fi.DTYPES[o], None, 0.0, None)
 
 
+def _prefill_fp8q(L, kv, q="e4m3", o="f16", hq=4, batch=2, qp=None, op=None, q_scale=1.0, qo_dev=None):
+    qo = np.array([0, 3, 7], np.int32)
+    return L.fi_batch_prefill_paged_fp8q(qp, fi.DTYPES[q], q_scale, qo_dev, qo.ctypes.data, batch, hq, ctypes.byref(kv),
+                                         1, op, fi.DTYPES[o], None, 0.0, None)
+
+
 def _err(L):
     return L.fi_last_error().decode()
 
@@ -170,6 +176,15 @@ DTYPE_REFUSALS = [
     ("single_prefill", dict(k="f16", v="bf16"), 1, "fi_single_prefill: k has dtype float16 but v has dtype bfloat16"),
     ("single_prefill", dict(k="e5m2fnuz"), 1, "fi_single_prefill: KV cache has dtype float8_e5m2fnuz"),
     ("single_prefill", dict(o="e4m3"), 1, "fi_single_prefill: o has dtype float8_e4m3fn"),
+    ("fp8q", dict(q="f16", o="f16"), 1, "fi_batch_prefill_paged_fp8q: q has dtype float16; this call takes an fp8 query"),
+    ("fp8q", dict(q="e4m3fnuz", o="f16"), 1, "q has dtype float8_e4m3fnuz; this call takes an fp8 query"),
+    ("fp8q", dict(q="e4m3", o="default"), 1, "o_dtype must be given for an fp8 query"),
+    ("fp8q", dict(q="e4m3", o="e5m2"), 1, "o has dtype float8_e5m2; an fp8 output is not supported"),
+    ("fp8q", dict(q="e5m2", o="bf16", k="e4m3", v="e5m2"), 1, "k has dtype float8_e4m3fn but v has dtype float8_e5m2"),
+    ("fp8q", dict(q="e4m3", o="f16", k="f16"), 1,
+     "q has dtype float8_e4m3fn but the KV cache has dtype float16; an fp8 query needs an fp8 KV cache"),
+    ("fp8q", dict(q="e4m3", o="f16", k="u8"), 1, "KV cache has dtype uint8, which has no float interpretation"),
+    ("fp8q", dict(q="e4m3", o="f16", k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
 ]
 
 
@@ -184,6 +199,9 @@ def test_dtype_refusals(L, call, kw, status, frag):
         st = _single(L, q=q, k=k, v=v, o=o)
     elif call == "single_prefill":
         st = _single_prefill(L, q=q, k=k, v=v, o=o)
+    elif call == "fp8q":
+        kv, keep = _kv(k, v)
+        st = _prefill_fp8q(L, kv, q=q, o=o)
     elif call == "ragged":
         kv, keep = _ragged(k, v)
         st = _prefill_ragged(L, kv, q=q, o=o)
@@ -281,6 +299,21 @@ def test_ragged_and_single_prefill_refusals(L):
     assert _single_prefill(L, qo_len=0, kv_len=0) == 0
     kv, keep = _ragged(ptrs=True)
     assert L.fi_batch_prefill_ragged(None, 1, None, None, 0, 4, ctypes.byref(kv), 1, None, 0, None, 0.0, None) == 0
+
+
+@no_gpu
+def test_fp8q_argument_refusals(L):
+    fake = 0x10000
+    kv, keep = _kv(ptrs=True)
+    assert _prefill_fp8q(L, kv, qp=fake, op=fake, q_scale=0.0, qo_dev=fake) == 3 and "q_scale=0" in _err(L)
+    assert _prefill_fp8q(L, kv, qp=fake, op=fake, q_scale=float("nan"), qo_dev=fake) == 3 and "q_scale" in _err(L)
+    assert _prefill_fp8q(L, kv, qp=fake, op=fake) == 3 and "qo_indptr and qo_indptr_h" in _err(L)
+    assert _prefill_fp8q(L, kv, qp=fake + 4, op=fake, qo_dev=fake) == 3 and "16-byte aligned" in _err(L)
+    kv2, keep2 = _kv(ptrs=True, d=80)
+    assert _prefill_fp8q(L, kv2, qp=fake, op=fake, qo_dev=fake) == 2 and "head_dim=80" in _err(L)
+    kv3, keep3 = _kv(ptrs=True, lpl=[5, 0])
+    assert _prefill_fp8q(L, kv3, qp=fake, op=fake, qo_dev=fake) == 3 and "last_page_len[1]=0" in _err(L)
+    assert _prefill_fp8q(L, kv, batch=0) == 0
 
 
 @no_gpu

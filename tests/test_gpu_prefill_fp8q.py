@@ -1,0 +1,119 @@
+"""GPU parity tests for batched paged prefill with an fp8 query, through the
+C ABI, against the float64 oracle.
+
+The query arrives as fp8 codes with a per-tensor q_scale that joins k_scale
+and sm_scale in the logit scale ("Enable Hopper FA3 FP8 attention in
+decode.py", flashinfer PR #2148, review comments on q_scale); the output is
+float16 or bfloat16.  S = Q K^T runs on the fp8 matrix cores with K kept in
+fp8, P V in float16, so the tolerances are those of the 2-byte path.
+
+Cases: both query formats against both cache formats, both output types,
+head_dim 64 and 128, GQA groups 1 to 8, page sizes 1 to 128, causal and not,
+ragged lengths that leave partial tiles; the causal prefill configuration (3)
+with its query quantised to e4m3, at full size (whole requests and sampled
+rows); requests without queries or keys; run-to-run and page-permutation
+determinism (bitwise).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+from workloads import make_config, make_paged
+from gpu_util import T2, assert_parity, paged_kv, say, upload
+from attention_paged_fp8_amd import fi
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8q(w: dict, d: dict, *, causal=True, kv=None):
+    T = int(w["qo_indptr"][-1])
+    o = torch.full((T, w["num_qo_heads"], w["head_dim"]), float("nan"), dtype=T2[w["o_dtype"]], device=d["q"].device)
+    lse = torch.full((T, w["num_qo_heads"]), float("nan"), dtype=torch.float32, device=d["q"].device)
+    if kv is None:
+        kv, keep = paged_kv(w, d)
+    fi.fi_batch_prefill_paged_fp8q(d["q"], d["qo_indptr"], kv, o, q_dtype=w["q_dtype"], q_scale=w["q_scale"],
+                                   causal=causal, lse=lse, qo_indptr_h=w["qo_indptr"])
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+SMALL = [
+    # (q, kvd, o, page, d, hq, hkv, qo, prefix, causal)
+    ("e4m3", "e4m3", "f16", 16, 128, 32, 8, (1, 37, 130, 64), (0, 100, 5, 300), True),
+    ("e4m3", "e4m3", "bf16", 16, 128, 32, 8, (1, 37, 130, 64), (0, 100, 5, 300), False),
+    ("e5m2", "e4m3", "f16", 64, 128, 16, 8, (200, 33), (70, 0), True),        # group 2
+    ("e4m3", "e5m2", "bf16", 4, 64, 8, 8, (129, 3, 257), (1, 64, 0), True),   # group 1
+    ("e5m2", "e5m2", "f16", 1, 64, 12, 4, (45, 90), (10, 0), True),           # group 3
+    ("e4m3", "e5m2", "f16", 32, 128, 64, 8, (100, 65), (40, 1), True),        # group 8
+    ("e5m2", "e4m3", "bf16", 128, 128, 32, 8, (70, 300), (400, 2), False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"q{c[0]}-{c[1]}-o{c[2]}-p{c[3]}-d{c[4]}-h{c[5]}x{c[6]}-c{int(c[9])}" for c in SMALL])
+def test_fp8q_small(gpu_device, case):
+    q, kvd, o, page, d_, hq, hkv, qo, prefix, causal = case
+    say("fp8q small", case)
+    w = make_paged(91, qo_lens=list(qo), prefix_lens=list(prefix), hq=hq, hkv=hkv, d=d_, page=page, q=q, kvd=kvd,
+                   o=o, extra_pages=2)
+    dv = upload(w, gpu_device)
+    og, lg = run_fp8q(w, dv, causal=causal)
+    o_ref, l_ref = OA.batch_prefill(w, causal=causal)
+    assert_parity(og, lg, o_ref, l_ref, o, str(case))
+
+
+def _config3_fp8q():
+    """The causal prefill configuration (3) with its query quantised to e4m3
+    (per-tensor scale): the same lengths, pages and draws."""
+    return make_config(3, q="e4m3")
+
+
+def test_config3_fp8q_full_size(gpu_device):
+    say("config3 fp8q")
+    w = _config3_fp8q()
+    d = upload(w, gpu_device)
+    og, lg = run_fp8q(w, d)
+    og2, lg2 = run_fp8q(w, d)
+    assert np.array_equal(og, og2) and np.array_equal(lg, lg2), "fp8-query prefill is not deterministic"
+    reqs = [0, 9]
+    o_ref, l_ref = OA.batch_prefill(w, causal=True, requests=reqs)
+    qi = w["qo_indptr"]
+    for i in reqs:
+        a, b = int(qi[i]), int(qi[i + 1])
+        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"config 3 fp8q request {i}")
+    rng = np.random.default_rng(1)
+    toks, heads = [], []
+    for i in range(len(w["qo_lens"])):
+        a, b = int(qi[i]), int(qi[i + 1])
+        for t in {a, b - 1, int(rng.integers(a, b))}:
+            for h in rng.choice(32, 3, replace=False):
+                toks.append(t)
+                heads.append(int(h))
+    o_s, l_s = OA.attention_rows(w, toks, heads, causal=True)
+    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "config 3 fp8q sampled rows")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8q_requests_without_queries_or_keys(gpu_device, causal):
+    say("fp8q empty requests", causal)
+    w = make_paged(93, qo_lens=[0, 40, 13, 0, 7, 50], kv_lens=[5, 0, 200, 0, 7, 20], hq=8, hkv=2, d=64, page=16,
+                   q="e5m2", kvd="e4m3", o="bf16")
+    dv = upload(w, gpu_device)
+    o, l = run_fp8q(w, dv, causal=causal)
+    assert np.all(o[0:40] == 0) and np.all(np.isneginf(l[0:40]))
+    o_ref, l_ref = OA.batch_prefill(w, causal=causal)
+    assert_parity(o, l, o_ref, l_ref, "bf16", "fp8q empty requests")
+
+
+def test_fp8q_page_permutation_bitwise(gpu_device):
+    say("fp8q page permutation")
+    w = make_paged(95, qo_lens=[300, 17, 129], prefix_lens=[700, 0, 63], hq=32, hkv=8, d=128, page=16, q="e4m3",
+                   kvd="e4m3", o="f16", extra_pages=20)
+    d = upload(w, gpu_device)
+    o1, l1 = run_fp8q(w, d)
+    P = w["k_pool"].shape[0]
+    perm = np.random.default_rng(6).permutation(P)
+    inv = np.argsort(perm)
+    w2 = dict(w, k_pool=w["k_pool"][perm], v_pool=w["v_pool"][perm], indices=inv[w["indices"]].astype(np.int32))
+    o2, l2 = run_fp8q(w2, upload(w2, gpu_device))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

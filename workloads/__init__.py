@@ -170,19 +170,21 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
     )
 
 
-def make_config(cfg_id: int, kvd: str | None = None) -> dict:
+def make_config(cfg_id: int, kvd: str | None = None, q: str | None = None) -> dict:
     """The workload of one measured configuration (seed = configuration number;
-    configuration 5 takes its KV dtype as an argument, one of f16, bf16, e4m3)."""
+    configuration 5 takes its KV dtype as an argument, one of f16, bf16, e4m3).
+    ``q`` replaces the query dtype (e.g. "e4m3": the same draws quantised with
+    a per-tensor scale); the name then says so."""
     c = CONFIGS[cfg_id]
     kvd_eff = kvd if kvd is not None else (c["kvd"] if isinstance(c["kvd"], str) else c["kvd"][-1])
-    common = dict(hq=c["hq"], hkv=c["hkv"], d=c["d"], page=c["page"], q=c["q"], kvd=kvd_eff, o=c["o"],
+    common = dict(hq=c["hq"], hkv=c["hkv"], d=c["d"], page=c["page"], q=q or c["q"], kvd=kvd_eff, o=c["o"],
                   contiguous=c["contiguous"], batch=c["batch"])
     if c["kind"] == "prefill":
         w = make_paged(cfg_id, qo_range=c["qo"], prefix_range=c["prefix"], **common)
     else:
         w = make_paged(cfg_id, kv_range=c["kv"], **common)
     w["config"] = cfg_id
-    w["name"] = c["name"]
+    w["name"] = c["name"] + (f"_q{q}" if q else "")
     w["kind"] = c["kind"]
     return w
 
