@@ -581,8 +581,8 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
 
 fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
                                       const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
-                                      const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
-                                      float sm_scale, void* stream) {
+                                      const fi_paged_kv* kv, int32_t causal, int32_t pv_fp8, void* o,
+                                      fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
   static const char* fn = "fi_batch_prefill_paged_fp8q";
   if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
   fi_status st = check_dtypes_fp8q(fn, q_dtype, o_dtype, kv->k_dtype, kv->v_dtype);
@@ -617,6 +617,7 @@ fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_s
   p.last_page_len = kv->last_page_len;
   p.page_shift = ilog2(kv->page_size);
   p.page_size = kv->page_size;
+  p.pv_fp8 = pv_fp8 ? 1 : 0;
   // q_scale joins k_scale in the logit scale (both multiply the fp32 products)
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * q_scale, kv->v_scale, false,

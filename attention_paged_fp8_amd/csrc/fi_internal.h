@@ -99,6 +99,7 @@ struct PrefillParams {
   int32_t q_per_wg;       // 32 * kPrefillWaves / heads_per_wg query tokens per workgroup
   int32_t n_qblocks;      // grid.y when n_items == 0
   int32_t causal;
+  int32_t pv_fp8;         // fp8 queries: P rounded to e4m3 and P V on the fp8 MFMA
   float scale_log2;
   float v_scale;
   // Dispatch order: when n_items > 0, workgroup x serves pair order[x / (kv

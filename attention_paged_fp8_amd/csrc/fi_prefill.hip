@@ -49,16 +49,20 @@
 namespace fi {
 
 // Q8: an fp8 query; K stays fp8 in LDS and S = K Q^T runs on the fp8 MFMA,
-// while P V runs in fp16 (QBF16 is then false).
-template <bool QBF16, int KVF, bool OBF16, int D, bool Q8>
+// while P V runs in fp16 (QBF16 is then false).  P8 (with Q8): V stays fp8
+// in LDS too, the probabilities are rounded to e4m3 and P V also runs on the
+// fp8 MFMA; the output is then normalised by the fp32 sum.
+template <bool QBF16, int KVF, bool OBF16, int D, bool Q8, bool P8 = false>
 struct PrefillCfg {
   static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
   static_assert(!Q8 || kFp8, "an fp8 query needs an fp8 KV cache");
+  static_assert(!P8 || Q8, "fp8 P V needs the fp8 query path");
+  static constexpr bool kP8 = P8;
   // The output is normalised by the sum of the probabilities as rounded for
   // the PV MFMA.  fp16 rounds at 2^-11 and that sum also gives the
   // log-sum-exp; bf16 rounds at 2^-9, so its log-sum-exp uses a separate sum
   // of the fp32 values.
-  static constexpr bool kF32Lse = QBF16;
+  static constexpr bool kF32Lse = QBF16 || P8;
   static constexpr int KVB = kFp8 ? 1 : 2;
   static constexpr int TK = 64;                 // keys per tile
   static constexpr int DB = D * KVB;            // stored bytes of a row
@@ -67,7 +71,10 @@ struct PrefillCfg {
   // D + 16, an odd multiple of 16 bytes, so the 16-byte reads of 16
   // consecutive rows fall in distinct bank groups
   static constexpr int KP = Q8 ? D + 16 : ROW + 16;
-  static constexpr int VP = (ROW + 191) / 256 * 256 + 64;  // V tile pitch, 64 mod 256 bytes
+  // V tile pitch: 64 mod 256 bytes for 2-byte rows; raw fp8 rows (P8) take
+  // D + 32, an odd multiple of 32 bytes, so 8 consecutive rows fall in distinct
+  // 32-byte bank groups for the transposed byte reads
+  static constexpr int VP = P8 ? D + 32 : (ROW + 191) / 256 * 256 + 64;
   static constexpr int KTILE = TK * KP;
   static constexpr int VTILE = TK * VP;
   // two K slots, then two V slots
@@ -120,6 +127,19 @@ __device__ __forceinline__ void schedule_qk8_exp() {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 }
+// Block 2 with the fp8 PV MFMA: each MFMA with its four transposed byte
+// reads and a share of the row max work, then the K stores.
+template <int NPV>
+__device__ __forceinline__ void schedule_pv8_max() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+}
 template <int NPV>
 __device__ __forceinline__ void schedule_pv_max() {
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -135,11 +155,11 @@ __device__ __forceinline__ void schedule_pv_max() {
 // RAGGED: K/V rows are contiguous per request -- token t of request b is row
 // indptr[b] + t of the pools (or row t when indptr is NULL) -- so the page
 // walk reduces to an addition and no index is loaded.
-template <int QF, int KVF, bool OBF16, int D, bool RAGGED>
+template <int QF, int KVF, bool OBF16, int D, bool RAGGED, bool P8>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const PrefillParams p) {
   constexpr bool QBF16 = QF == FMT_BF16;
   constexpr bool Q8 = QF == FMT_E4M3 || QF == FMT_E5M2;
-  using Cfg = PrefillCfg<QBF16, KVF, OBF16, D, Q8>;
+  using Cfg = PrefillCfg<QBF16, KVF, OBF16, D, Q8, P8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
   const int nsg = p.group / p.heads_per_wg;
@@ -272,12 +292,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       if (ld_on(j)) f.v[j] = load16(vb + goff[j]);
   };
   // store rows into an LDS slot in the dim_of order, fp8 widened to q's type
-  // (raw: fp8 K rows for the fp8 MFMA, as loaded)
-  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw) {
+  // (raw: fp8 rows for the fp8 MFMA, as loaded; fp8 V rows (P8) go to row
+  // v8_row(t), which lists each 16-token block as tokens 0-3, 8-11, 4-7,
+  // 12-15, so that every transposed read of P V takes 8 consecutive rows)
+  auto v8_row = [](int t) { return (t & ~15) | (t & 3) | (((t >> 3) & 1) << 2) | (((t >> 2) & 1) << 3); };
+  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw, auto vperm) {
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j) {
       if (!ld_on(j)) continue;
-      uint8_t* d = slot + ld_row[j] * pitch;
+      uint8_t* d = slot + (decltype(vperm)::value ? v8_row(ld_row[j]) : ld_row[j]) * pitch;
       if constexpr (decltype(raw)::value) {
         *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = r[j];
       } else if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
@@ -288,8 +311,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       }
     }
   };
-  auto store_k = [&](const Fetch& f, uint8_t* slot) { store_rows(f.k, slot, Cfg::KP, std::integral_constant<bool, Q8>{}); };
-  auto store_v = [&](const Fetch& f, uint8_t* slot) { store_rows(f.v, slot, Cfg::VP, std::false_type{}); };
+  auto store_k = [&](const Fetch& f, uint8_t* slot) {
+    store_rows(f.k, slot, Cfg::KP, std::integral_constant<bool, Q8>{}, std::false_type{});
+  };
+  auto store_v = [&](const Fetch& f, uint8_t* slot) {
+    store_rows(f.v, slot, Cfg::VP, std::integral_constant<bool, P8>{}, std::integral_constant<bool, P8>{});
+  };
 
   // ---- per-wave attention state --------------------------------------------
   float m_run = kNegInf;  // running max (base-2 scaled logits), updated lazily
@@ -307,6 +334,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   // lanes 4r..4r+3 name the four 8-byte pieces of row r of a 16-column block.
   const int k_base = rho * Cfg::KP + (Q8 ? 32 : D) * hh;
   const int v_base = (4 * hh + ((rho & 15) >> 2)) * Cfg::VP + 32 * (rho >> 4) + 8 * (rho & 3);
+  // fp8 V^T (P8) transposed byte reads: in 16-lane group G = lane / 16 (hh =
+  // G / 2), lanes 2r and 2r+1 name the two 8-byte halves of row 8hh + r of a
+  // 16-row block at dimensions 16(G % 2) .. +15 of a 32-dimension block
+  const int v8_base = (8 * hh + ((rho & 15) >> 1)) * Cfg::VP + 16 * (rho >> 4) + 8 * (rho & 1);
 
   // S^T = K Q^T for one tile, two 32-token halves; lane (hh, rho) then holds
   // keys 32*sub + 8*(i/4) + 4*hh + i%4 of row rho
@@ -373,6 +404,29 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   // (slot u = tokens 16u .. 16u+15), and their row sums
   auto exp_pack = [&](const f32x16_t(&s)[2], float m_use, uint4(&pop)[4]) {
     float rsum = 0.f, psum = 0.f;
+    if constexpr (P8) {
+      // e4m3 probabilities, byte 16*sub + i of the P^T operand holding S(j)
+      // register s[sub][i] (keys 32sub + 8(i/4) + 4hh + i%4)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        uint32_t wds[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int i0 = 4 * d;
+          const float e0 = fast_exp2(__builtin_fmaf(s[sub][i0], p.scale_log2, -m_use));
+          const float e1 = fast_exp2(__builtin_fmaf(s[sub][i0 + 1], p.scale_log2, -m_use));
+          const float e2 = fast_exp2(__builtin_fmaf(s[sub][i0 + 2], p.scale_log2, -m_use));
+          const float e3 = fast_exp2(__builtin_fmaf(s[sub][i0 + 3], p.scale_log2, -m_use));
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+          wds[d] = (uint32_t)wd;
+          psum += (e0 + e1) + (e2 + e3);
+        }
+        pop[sub] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+      }
+      l_run += psum;
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t wds[4];
@@ -394,6 +448,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   // over tokens r0..r0+3 and r0+8..r0+11 (r0 = 32*(u/2) + 16*(u%2) + 4*hh),
   // the order its P^T slots hold: two transposed LDS reads of 4 rows each.
   auto pv = [&](const uint8_t* vslot, const uint4(&pop)[4]) {
+    if constexpr (P8) {
+      // O^T += V^T P^T on the fp8 MFMA, one per 32 dimensions: A byte 8r + b
+      // is dimension 32db + lane%32 of token 32(r/2) + 16(r%2) + 8(b/4) + 4hh
+      // + b%4, the key order of the P^T bytes
+      const uint8_t* vl = vslot + v8_base;
+#pragma unroll
+      for (int db = 0; db < Cfg::NDB; ++db) {
+        uint2 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = lds_tr8(vl + (32 * (r >> 1) + 16 * (r & 1)) * Cfg::VP + 32 * db);
+        acc[db] = mfma32x32x64_f8<KVF, FMT_E4M3>(make_uint4(x[0].x, x[0].y, x[1].x, x[1].y),
+                                                  make_uint4(x[2].x, x[2].y, x[3].x, x[3].y), pop[0], pop[1], acc[db]);
+      }
+      return;
+    }
     const uint8_t* vl = vslot + v_base;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -432,7 +501,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       // the probabilities are materialised here, beside the QK products,
       // rather than sunk past the mask branch into the PV block (emits nothing)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pop[u].x), "v"(pop[u].y), "v"(pop[u].z), "v"(pop[u].w));
+      for (int u = 0; u < (P8 ? 2 : 4); ++u) asm volatile("" ::"v"(pop[u].x), "v"(pop[u].y), "v"(pop[u].z), "v"(pop[u].w));
       if constexpr (Q8)
         schedule_qk8_exp<2 * Cfg::NS8>();
       else
@@ -441,7 +510,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       pv(v_this, pop);
       const float mx = row_max(sn);
       store_k(f, k_this);
-      schedule_pv_max<4 * Cfg::NDB>();
+      if constexpr (P8)
+        schedule_pv8_max<Cfg::NDB>();
+      else
+        schedule_pv_max<4 * Cfg::NDB>();
       m_use = rebase(mx);  // after P(j) V(j): a rescale applies to it
     } else {
       store_k(f, k_this);
@@ -509,13 +581,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   lr_run = sum_half_swap(lr_run);
   l_run = Cfg::kF32Lse ? sum_half_swap(l_run) : lr_run;
   if (!row_ok) return;
-  const float inv = (lr_run > 0.f) ? p.v_scale / lr_run : 0.f;
+  const float lnorm = P8 ? l_run : lr_run;  // fp8 probabilities: the fp32 sum
+  const float inv = (lnorm > 0.f) ? p.v_scale / lnorm : 0.f;
   uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(q_begin + qpos) * p.num_qo_heads + hq) * D;
 #pragma unroll
   for (int db = 0; db < Cfg::NDB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = Cfg::dim_of(32 * db + 8 * i4 + 4 * hh);  // 4 positions, 4 consecutive dimensions
+      // 4 positions, 4 consecutive dimensions (fp8 V^T rows are dimensions)
+      const int d = P8 ? 32 * db + 8 * i4 + 4 * hh : Cfg::dim_of(32 * db + 8 * i4 + 4 * hh);
       *reinterpret_cast<uint2*>(op + d) = make_uint2(pack2<OBF16>(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv),
                                                      pack2<OBF16>(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv));
     }
@@ -529,11 +603,19 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int batch, bool ragge
   const int nsg = p.group / p.heads_per_wg;
   const dim3 grid = (p.n_items > 0) ? dim3(p.n_items * p.num_kv_heads * nsg, 1)
                                     : dim3(batch * p.num_kv_heads * nsg, p.n_qblocks);
-  if (ragged) {
-    if constexpr (QF == FMT_E4M3 || QF == FMT_E5M2) return hipErrorInvalidValue;  // fp8 queries: paged calls only
-    else hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
-  } else
-    hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  if constexpr (QF == FMT_E4M3 || QF == FMT_E5M2) {  // fp8 queries: paged calls only
+    if (ragged) return hipErrorInvalidValue;
+    if (p.pv_fp8)
+      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  } else {
+    if (p.pv_fp8) return hipErrorInvalidValue;
+    if (ragged)
+      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, true, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -101,8 +101,8 @@ def lib() -> ctypes.CDLL:
     L.fi_batch_prefill_paged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(PagedKV), i32, vp, en, vp, f32, vp,
                                          sz, vp]
     L.fi_batch_prefill_paged_fp8q.restype = en
-    L.fi_batch_prefill_paged_fp8q.argtypes = [vp, en, f32, vp, vp, i32, i32, ctypes.POINTER(PagedKV), i32, vp, en, vp,
-                                              f32, vp]
+    L.fi_batch_prefill_paged_fp8q.argtypes = [vp, en, f32, vp, vp, i32, i32, ctypes.POINTER(PagedKV), i32, i32, vp, en,
+                                              vp, f32, vp]
     L.fi_batch_prefill_ragged.restype = en
     L.fi_batch_prefill_ragged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(RaggedKV), i32, vp, en, vp, f32,
                                           vp]
@@ -216,15 +216,16 @@ def fi_batch_prefill_paged(q, qo_indptr, kv: PagedKV, o, *, causal=True, q_dtype
 
 
 def fi_batch_prefill_paged_fp8q(q, qo_indptr, kv: PagedKV, o, *, q_dtype, o_dtype=None, q_scale=1.0, causal=True,
-                                lse=None, sm_scale=0.0, qo_indptr_h=None, batch=None, num_qo_heads=None, stream=None):
+                                pv_fp8=False, lse=None, sm_scale=0.0, qo_indptr_h=None, batch=None, num_qo_heads=None,
+                                stream=None):
     """q [total_q, H_qo, D] fp8 codes (a float8 tensor, or uint8 with q_dtype
     naming the format); o [total_q, H_qo, D] float16 or bfloat16."""
     qh = _host_i32(qo_indptr_h if qo_indptr_h is not None else qo_indptr)
     st = lib().fi_batch_prefill_paged_fp8q(
         _ptr(q), _dt(q_dtype), float(q_scale), _ptr(qo_indptr), qh.data_ptr(),
         int(batch if batch is not None else qh.numel() - 1), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
-        ctypes.byref(kv), 1 if causal else 0, _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse),
-        float(sm_scale), _stream(stream, q, o))
+        ctypes.byref(kv), 1 if causal else 0, 1 if pv_fp8 else 0, _ptr(o),
+        _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale), _stream(stream, q, o))
     check(st)
     return o
 

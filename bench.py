@@ -146,10 +146,11 @@ def run_decode_bench(steps, warmup, copies, cfg=2, kvd=None):
     return w, wall_ms, ev
 
 
-def run_prefill_bench(steps, warmup, ragged=False, fp8q=False):
+def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False):
     """The causal prefill workload through the paged call, or (ragged) the
     same K/V values stored contiguously per request through the ragged call,
-    or (fp8q) with its query quantised to e4m3 through the fp8-query call."""
+    or (fp8q) with its query quantised to e4m3 through the fp8-query call
+    (pv_fp8: P V on the fp8 MFMA as well)."""
     import torch
 
     from attention_paged_fp8_amd import fi
@@ -171,8 +172,8 @@ def run_prefill_bench(steps, warmup, ragged=False, fp8q=False):
     def step(i):
         if fp8q:
             fi.fi_batch_prefill_paged_fp8q(q, idx["qo_indptr"], kvs[0], o, q_dtype="e4m3", q_scale=w["q_scale"],
-                                           o_dtype=w["o_dtype"], causal=True, lse=lse, qo_indptr_h=w["qo_indptr"],
-                                           stream=stream)
+                                           o_dtype=w["o_dtype"], causal=True, pv_fp8=pv_fp8, lse=lse,
+                                           qo_indptr_h=w["qo_indptr"], stream=stream)
         elif ragged:
             fi.fi_batch_prefill_ragged(q, idx["qo_indptr"], rkv, o, causal=True, lse=lse,
                                        qo_indptr_h=w["qo_indptr"], stream=stream)
@@ -357,6 +358,12 @@ def main():
                                     "note": "QK on the fp8 MFMA, PV in f16"}
             print(f"# prefill, fp8 query: events median {f_ms * 1e3:.1f} us -> {flops / (f_ms * 1e-3) / 1e12:.1f} "
                   "TFLOP/s", file=sys.stderr, flush=True)
+            _, _, g_ev = run_prefill_bench(args.prefill_steps, 3, fp8q=True, pv_fp8=True)
+            g_ms = float(np.median(g_ev))
+            prefill["fp8_query_fp8_pv"] = {"ms": round(g_ms, 5), "tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
+                                           "note": "QK and PV on the fp8 MFMA, P rounded to e4m3"}
+            print(f"# prefill, fp8 query and fp8 P V: events median {g_ms * 1e3:.1f} us -> "
+                  f"{flops / (g_ms * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     extra, copy_gbs = None, None
     if args.only == "all" and not args.no_extra:

@@ -175,16 +175,22 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
  *            query format)
  *   o_dtype  FI_F16 or FI_BF16, given explicitly (FI_DTYPE_DEFAULT, the
  *            query's own dtype, is refused)
+ *   pv_fp8   0: P V in float16 (P rounded to float16, V widened exactly);
+ *            nonzero: P rounded to e4m3 (round to nearest even) and P V on
+ *            the fp8 matrix cores with V staying fp8 ([A] and [B]: the FA3
+ *            fp8 path quantises the probabilities for the second product)
  * Other arguments, layouts, the causal mask and results as
  * fi_batch_prefill_paged.  S = Q K^T runs on the fp8 matrix cores with K
  * staying fp8 from HBM to the MFMA; the products are exact and summed in
- * fp32 as in the 2-byte path; P V runs in float16 (P rounded to float16, V
- * widened exactly), so the result matches the 2-byte path to the same
- * tolerance. */
+ * fp32 as in the 2-byte path.  With pv_fp8 = 0 the result matches the 2-byte
+ * path to the same tolerance.  With pv_fp8 set, each probability carries a
+ * relative rounding error of at most 2^-4 (absolute 2^-10 of the row's
+ * reference maximum below 2^-6 of it); the output is normalised by the fp32
+ * sum of the unrounded probabilities, which also gives lse. */
 fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
                                       const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
-                                      const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
-                                      float sm_scale, void* stream);
+                                      const fi_paged_kv* kv, int32_t causal, int32_t pv_fp8, void* o,
+                                      fi_dtype o_dtype, float* lse, float sm_scale, void* stream);
 
 /* K/V held contiguously per request ("ragged"): request i owns rows
  * indptr[i] .. indptr[i+1]-1 of each pool, row r of kv head g at element

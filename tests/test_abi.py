@@ -132,7 +132,7 @@ def _single_prefill(L, q="f16", k="e4m3", v=None, o="default", d=64, hq=4, hkv=2
 def _prefill_fp8q(L, kv, q="e4m3", o="f16", hq=4, batch=2, qp=None, op=None, q_scale=1.0, qo_dev=None):
     qo = np.array([0, 3, 7], np.int32)
     return L.fi_batch_prefill_paged_fp8q(qp, fi.DTYPES[q], q_scale, qo_dev, qo.ctypes.data, batch, hq, ctypes.byref(kv),
-                                         1, op, fi.DTYPES[o], None, 0.0, None)
+                                         1, 0, op, fi.DTYPES[o], None, 0.0, None)
 
 
 def _err(L):
