@@ -46,7 +46,7 @@ import numpy as np
 from .fp8 import fp8_table
 
 TWO_BYTE = ("f16", "bf16")
-FP8 = ("e4m3", "e5m2")
+FP8 = ("e4m3", "e5m2", "e4m3fnuz", "e5m2fnuz")
 
 
 # --------------------------------------------------------------------------

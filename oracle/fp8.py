@@ -1,4 +1,5 @@
-"""Exact 256-entry decode tables for the OCP 8-bit float formats.
+"""Exact 256-entry decode tables for the OCP 8-bit float formats and their
+fnuz variants.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and its
 Python binding) may import this package; only the tests, the smoke check and the
@@ -19,6 +20,12 @@ floating point specification, which the pages name but do not restate:
     with mantissa 0 is +-inf, with mantissa != 0 NaN; max finite 57344.
 Both have signed zero and subnormals (exponent field 0).
 
+The gfx942 "fnuz" variants (same page: a KV cache may also be fnuz fp8 there;
+biases 8 and 16) follow the fnuz convention, which the pages also leave to
+the format's definition: no infinities, no negative zero, and the single NaN
+encoding 0x80 (sign bit alone); every other code decodes with the formula
+below, so e4m3fnuz reaches 240 at 0x7F and e5m2fnuz 57344 at 0x7F.
+
 Two constructions that share nothing but the format parameters:
   * ``table_closed_form``: decodes each code's bit fields with the textbook
     formula (-1)^s * 2^(e-bias) * (1 + m/2^M), subnormal 2^(1-bias) * m/2^M.
@@ -36,6 +43,8 @@ import numpy as np
 FORMATS = {
     "e4m3": (4, 3, 7),
     "e5m2": (5, 2, 15),
+    "e4m3fnuz": (4, 3, 8),
+    "e5m2fnuz": (5, 2, 16),
 }
 
 
@@ -46,6 +55,9 @@ def _is_special(fmt: str, code: int) -> str | None:
     e = (code >> mbits) & ((1 << ebits) - 1)
     m = code & ((1 << mbits) - 1)
     emax_field = (1 << ebits) - 1
+    if fmt.endswith("fnuz"):
+        # fnuz: no infinities and no negative zero; the one NaN is 0x80
+        return "nan" if code == 0x80 else None
     if fmt == "e4m3":
         # OCP E4M3: only the all-ones exponent *and* all-ones mantissa is NaN.
         if e == emax_field and m == (1 << mbits) - 1:

@@ -37,7 +37,7 @@ def _same(a, b):
     return a == b and math.copysign(1, a) == math.copysign(1, b)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e4m3fnuz", "e5m2fnuz"])
 def test_two_constructions_agree(fmt):
     a = fp8.table_closed_form(fmt)
     b = fp8.table_ulp_ladder(fmt)
@@ -53,7 +53,8 @@ def test_anchor_codes():
         assert _same(got, val), (fmt, hex(code), got, val)
 
 
-@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2),
+                                     ("e4m3fnuz", torch.float8_e4m3fnuz), ("e5m2fnuz", torch.float8_e5m2fnuz)])
 def test_library_cast_agrees(fmt, tdt):
     ref = torch.arange(256, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
     t = fp8.fp8_table(fmt)
@@ -81,7 +82,7 @@ def test_denormals_present_and_ordered():
         assert np.all(np.diff(pos) > 0)  # magnitudes increase with the code
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e4m3fnuz", "e5m2fnuz"])
 def test_every_finite_code_is_exact_in_2byte_types(fmt):
     """Every finite fp8 value is exactly an fp16 and a bf16 value, so a kernel
     may widen the raw code into q's 2-byte type with no rounding."""
@@ -95,3 +96,21 @@ def test_every_finite_code_is_exact_in_2byte_types(fmt):
 def test_max_finite():
     assert fp8.max_finite("e4m3") == 448.0
     assert fp8.max_finite("e5m2") == 57344.0
+    assert fp8.max_finite("e4m3fnuz") == 240.0
+    assert fp8.max_finite("e5m2fnuz") == 57344.0
+
+
+def test_fnuz_with_the_ocp_bias_is_caught():
+    """Negative control for the fnuz tables: the page's latent vec_cast bug
+    decodes fnuz with the OCP bias (2x too large); the anchors must reject it."""
+    for fmt, ocp_bias in (("e4m3fnuz", 7), ("e5m2fnuz", 15)):
+        wrong = fp8.table_closed_form(fmt, bias=ocp_bias)
+        bad = [c for f, c, v in _anchors() if f == fmt and not _same(wrong[c], v)]
+        assert bad, fmt
+
+
+def test_fnuz_specials():
+    for fmt in ("e4m3fnuz", "e5m2fnuz"):
+        t = fp8.fp8_table(fmt)
+        assert np.isnan(t[0x80]) and np.sum(np.isnan(t)) == 1 and np.all(np.isfinite(t[~np.isnan(t)]))
+        assert not np.any(np.signbit(t[np.isfinite(t) & (t == 0)]))  # no negative zero

@@ -25,23 +25,25 @@ Draw order for one workload (numpy default_rng(seed)):
      x / scale clamped to +-max finite, cast round-to-nearest-even.  2-byte:
      cast directly, scale 1.
   5. slots past last_page_len, and unreferenced pages, are poisoned with a NaN
-     encoding (0x7F for fp8, the canonical quiet NaN for 2-byte types), so an
-     out-of-range read shows up as a non-finite output.
+     encoding (0x7F for OCP fp8, 0x80 for fnuz fp8, the canonical quiet NaN for
+     2-byte types), so an out-of-range read shows up as a non-finite output.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0, "e4m3fnuz": 240.0, "e5m2fnuz": 57344.0}
 _TORCH = {
     "f16": torch.float16,
     "bf16": torch.bfloat16,
     "e4m3": torch.float8_e4m3fn,
     "e5m2": torch.float8_e5m2,
+    "e4m3fnuz": torch.float8_e4m3fnuz,
+    "e5m2fnuz": torch.float8_e5m2fnuz,
 }
-NAN_BITS = {"e4m3": 0x7F, "e5m2": 0x7F, "f16": 0x7E00, "bf16": 0x7FC0}
-ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1}
+NAN_BITS = {"e4m3": 0x7F, "e5m2": 0x7F, "e4m3fnuz": 0x80, "e5m2fnuz": 0x80, "f16": 0x7E00, "bf16": 0x7FC0}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e4m3fnuz": 1, "e5m2fnuz": 1}
 
 # The five measured configurations.
 CONFIGS = {
