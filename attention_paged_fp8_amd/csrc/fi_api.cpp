@@ -79,12 +79,12 @@ fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_d
   if (k == FI_I8 || k == FI_U8)
     return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be float16, "
                 "bfloat16, float8_e4m3fn or float8_e5m2", dtype_name(k));
-  if (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ)
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; this library decodes OCP "
-                "float8_e4m3fn / float8_e5m2", dtype_name(k));
-  if (!is_2byte(k) && !is_ocp_fp8(k))
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s; KV must be float16, bfloat16, float8_e4m3fn or float8_e5m2",
-                dtype_name(k));
+  if (prefill && (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ))
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; fnuz caches are read by the "
+                "decode calls only (prefill takes float8_e4m3fn / float8_e5m2)", dtype_name(k));
+  if (!is_2byte(k) && !is_any_fp8(k))
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s; KV must be float16, bfloat16, float8_e4m3fn or float8_e5m2 "
+                "(decode also float8_e4m3fnuz / float8_e5m2fnuz)", dtype_name(k));
   if (prefill && is_2byte(k) && k != q)
     return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; prefill needs a 2-byte KV cache of the "
                 "query's dtype (fp8 KV is widened on load)", dtype_name(q), dtype_name(k));
@@ -316,6 +316,11 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
                 "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
   if (need > 0 && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
+  // e4m3fnuz codes are widened to value * 2^-7 (exactly); the 2^7 joins the scales
+  if (kv_dtype == FI_F8_E4M3_FNUZ) {
+    k_scale *= 128.f;
+    v_scale *= 128.f;
+  }
   p.scale_log2 = scale * k_scale * fi::kLog2eHost;
   p.v_scale = v_scale;
   float* ws = reinterpret_cast<float*>(workspace);
@@ -710,7 +715,9 @@ fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, con
 
 fi_status fi_fp8_widen(const uint8_t* codes, int64_t n, fi_dtype src, fi_dtype dst, void* out, void* stream) {
   static const char* fn = "fi_fp8_widen";
-  if (!is_ocp_fp8(src)) return fail(FI_E_DTYPE, fn, "src has dtype %s; src must be float8_e4m3fn or float8_e5m2", dtype_name(src));
+  if (!is_any_fp8(src))
+    return fail(FI_E_DTYPE, fn, "src has dtype %s; src must be float8_e4m3fn, float8_e5m2, float8_e4m3fnuz or "
+                "float8_e5m2fnuz", dtype_name(src));
   if (!is_2byte(dst)) return fail(FI_E_DTYPE, fn, "dst has dtype %s; dst must be float16 or bfloat16", dtype_name(dst));
   if (n < 0) return fail(FI_E_SHAPE, fn, "n=%lld is negative", (long long)n);
   if (n == 0) return FI_OK;

@@ -38,6 +38,7 @@
 // single rounding) or, when the request is split into several chunks, an fp32
 // partial (output, log-sum-exp) that merge_kernel combines.
 #include <atomic>
+#include <type_traits>
 
 #include "fi_device.hpp"
 
@@ -53,7 +54,7 @@ constexpr int kPidWindow = 1024;
 
 template <bool QBF16, int KVF, bool OBF16, int D>
 struct DecodeCfg {
-  static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
+  static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2 || KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ);
   // MFMA operand type: bf16 whenever q or a 2-byte cache is bf16.  An fp16
   // operand meeting a bf16 one is split exactly into bf16 hi + lo.
   static constexpr bool MBF16 = QBF16 || KVF == FMT_BF16;
@@ -513,6 +514,10 @@ __global__ __launch_bounds__(256) void widen_kernel(const uint8_t* codes, int64_
   for (int j = 0; j < 4; ++j)
     if (i + j < n) w |= (uint32_t)codes[i + j] << (8 * j);
   uint2 r = widen4<BF16, KVF>(w);
+  if constexpr (KVF == FMT_E4M3_FNUZ) {  // the attention kernels fold this 2^7 into their scales
+    r.x = pack2<BF16>(unpack2<BF16>(r.x).x * 128.f, unpack2<BF16>(r.x).y * 128.f);
+    r.y = pack2<BF16>(unpack2<BF16>(r.y).x * 128.f, unpack2<BF16>(r.y).y * 128.f);
+  }
   const uint16_t v[4] = {(uint16_t)(r.x & 0xffff), (uint16_t)(r.x >> 16), (uint16_t)(r.y & 0xffff),
                          (uint16_t)(r.y >> 16)};
 #pragma unroll
@@ -550,6 +555,8 @@ static hipError_t launch_decode_kv(const DecodeParams& p, int kv_fmt, int o_fmt,
     case FMT_F16: return launch_decode_o<QBF16, FMT_F16>(p, o_fmt, head_dim, batch, s);
     case FMT_BF16: return launch_decode_o<QBF16, FMT_BF16>(p, o_fmt, head_dim, batch, s);
     case FMT_E4M3: return launch_decode_o<QBF16, FMT_E4M3>(p, o_fmt, head_dim, batch, s);
+    case FMT_E4M3_FNUZ: return launch_decode_o<QBF16, FMT_E4M3_FNUZ>(p, o_fmt, head_dim, batch, s);
+    case FMT_E5M2_FNUZ: return launch_decode_o<QBF16, FMT_E5M2_FNUZ>(p, o_fmt, head_dim, batch, s);
     default: return launch_decode_o<QBF16, FMT_E5M2>(p, o_fmt, head_dim, batch, s);
   }
 }
@@ -575,6 +582,8 @@ static int occupancy_kv(int kv, int o, int d) {
     case FMT_F16: return occupancy_o<QBF16, FMT_F16>(o, d);
     case FMT_BF16: return occupancy_o<QBF16, FMT_BF16>(o, d);
     case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3>(o, d);
+    case FMT_E4M3_FNUZ: return occupancy_o<QBF16, FMT_E4M3_FNUZ>(o, d);
+    case FMT_E5M2_FNUZ: return occupancy_o<QBF16, FMT_E5M2_FNUZ>(o, d);
     default: return occupancy_o<QBF16, FMT_E5M2>(o, d);
   }
 }
@@ -592,9 +601,9 @@ int device_cus() {
 
 int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
   // cached per (device, instantiation): the values cannot change while the process runs
-  static std::atomic<int> cache[64][2][5][2][2];
+  static std::atomic<int> cache[64][2][10][2][2];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || kv_fmt < 0 || kv_fmt >= 10) return 0;
   std::atomic<int>& slot = cache[dev][q_fmt == FMT_BF16][kv_fmt][o_fmt == FMT_BF16][head_dim == 128];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
@@ -635,16 +644,18 @@ hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int ds
   const int64_t threads = (n + 3) / 4;
   dim3 grid((unsigned)((threads + 255) / 256));
   uint16_t* o = reinterpret_cast<uint16_t*>(out);
-  if (dst_fmt == FMT_BF16) {
-    if (src_fmt == FMT_E4M3)
-      hipLaunchKernelGGL((widen_kernel<true, FMT_E4M3>), grid, dim3(256), 0, s, codes, n, o);
+  auto go = [&](auto fmt) {
+    constexpr int KVF = decltype(fmt)::value;
+    if (dst_fmt == FMT_BF16)
+      hipLaunchKernelGGL((widen_kernel<true, KVF>), grid, dim3(256), 0, s, codes, n, o);
     else
-      hipLaunchKernelGGL((widen_kernel<true, FMT_E5M2>), grid, dim3(256), 0, s, codes, n, o);
-  } else {
-    if (src_fmt == FMT_E4M3)
-      hipLaunchKernelGGL((widen_kernel<false, FMT_E4M3>), grid, dim3(256), 0, s, codes, n, o);
-    else
-      hipLaunchKernelGGL((widen_kernel<false, FMT_E5M2>), grid, dim3(256), 0, s, codes, n, o);
+      hipLaunchKernelGGL((widen_kernel<false, KVF>), grid, dim3(256), 0, s, codes, n, o);
+  };
+  switch (src_fmt) {
+    case FMT_E4M3: go(std::integral_constant<int, FMT_E4M3>{}); break;
+    case FMT_E5M2: go(std::integral_constant<int, FMT_E5M2>{}); break;
+    case FMT_E4M3_FNUZ: go(std::integral_constant<int, FMT_E4M3_FNUZ>{}); break;
+    default: go(std::integral_constant<int, FMT_E5M2_FNUZ>{}); break;
   }
   return hipGetLastError();
 }

@@ -44,9 +44,53 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 // in fp16 and in bf16 (the oracle's tables test this), so no rounding occurs.
 // The k / v scales are not applied here but in fp32 (logit scale and output).
 // ---------------------------------------------------------------------------
+// fnuz codes (the gfx942 layouts: e4m3 bias 8, e5m2 bias 16, no inf, no -0,
+// NaN only at 0x80) have no conversion instruction on gfx950; their 2-byte
+// form is built from the bits, exactly.  A byte permute puts codes b0, b1 in
+// the high bytes of two 16-bit halves (x = b1 << 24 | b0 << 8), sign bits at
+// 15 and 31.  Then, per half:
+//  * e4m3fnuz: the 7 magnitude bits shifted to bits 13..7 form the fp16 of
+//    value * 2^-7 (exponent field e at bias 15 against the code's 8, and the
+//    subnormals line up too); the caller folds 2^7 into its scales.
+//  * e5m2fnuz: the 7 magnitude bits at 14..8 form the fp16 of 2 * value
+//    (bias 15 against 16), infinite where the code's exponent is 31; halving
+//    in the integer domain -- one exponent step down for exponent >= 2, a
+//    right shift below, i.e. max(sat(mag - 0x400), mag >> 1) -- gives the
+//    value exactly, the top binade 2^15 .. 57344 included.
+// The NaN code 0x80 reads as -0 (a cache holds it only as a NaN).
+// bf16 is then reached from fp16 exactly (every fnuz value has at most 4
+// significant bits and lies within fp16's range).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+template <int KVF>
+__device__ __forceinline__ uint32_t fnuz2_f16(uint32_t x) {
+  if constexpr (KVF == FMT_E4M3_FNUZ) {
+    return ((x >> 1) & 0x3F803F80u) | (x & 0x80008000u);
+  } else {
+    const u16x2_t mag = bitcast<u16x2_t>(x & 0x7F007F00u);
+    const u16x2_t step = {0x0400, 0x0400};
+    const u16x2_t r = __builtin_elementwise_max(__builtin_elementwise_sub_sat(mag, step), mag >> (unsigned short)1);
+    return bitcast<uint32_t>(r) | (x & 0x80008000u);
+  }
+}
+
+template <bool QBF16, int KVF>
+__device__ __forceinline__ uint2 fnuz4(uint32_t w) {
+  uint2 r = make_uint2(fnuz2_f16<KVF>(__builtin_amdgcn_perm(w, w, 0x010c000cu)),
+                       fnuz2_f16<KVF>(__builtin_amdgcn_perm(w, w, 0x030c020cu)));
+  if constexpr (QBF16) {
+    const f16x2_t a = bitcast<f16x2_t>(r.x), b = bitcast<f16x2_t>(r.y);
+    const bf16x2_t ab = {(__bf16)(float)a.x, (__bf16)(float)a.y};
+    const bf16x2_t bb = {(__bf16)(float)b.x, (__bf16)(float)b.y};
+    r = make_uint2(bitcast<uint32_t>(ab), bitcast<uint32_t>(bb));
+  }
+  return r;
+}
+
 // The two word_sel immediates must be compile-time constants.
 template <bool QBF16, int KVF>
 __device__ __forceinline__ uint2 widen4(uint32_t w) {
+  if constexpr (KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) return fnuz4<QBF16, KVF>(w);
   uint2 r;
   if constexpr (!QBF16) {
     if constexpr (KVF == FMT_E4M3) {

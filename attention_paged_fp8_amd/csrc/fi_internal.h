@@ -8,7 +8,7 @@
 namespace fi {
 
 // Stored element formats; the values match fi_dtype.
-enum Fmt : int { FMT_F16 = 1, FMT_BF16 = 2, FMT_E4M3 = 3, FMT_E5M2 = 4 };
+enum Fmt : int { FMT_F16 = 1, FMT_BF16 = 2, FMT_E4M3 = 3, FMT_E5M2 = 4, FMT_E4M3_FNUZ = 8, FMT_E5M2_FNUZ = 9 };
 
 constexpr int kDecodeWaves = 4;         // waves per decode workgroup, one (kv head, row slice) each
 constexpr int kDecodeStep = 16;         // tokens staged per step

@@ -19,7 +19,8 @@ MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head,
 and the same workload with its K/V stored contiguously per request through
 the ragged call; beside them the long-context split-KV decode (8 requests of 32k..128k tokens,
 64/8 heads, page 64, e5m2) and the batch-decode shapes with f16 q/o over f16,
-bf16 (mixed 2-byte) and e4m3 caches, a plain device copy's bandwidth for
+bf16 (mixed 2-byte) and e4m3 caches, the batch-decode workload over an e4m3fnuz
+cache, a plain device copy's bandwidth for
 context, and the float64 oracle timed on the host cores on a bounded sample.
 Roofline figures use the median of the per-call HIP events.
 """
@@ -42,7 +43,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS_16 = 2500.0   # MI355X dense fp16 / bf16 MFMA
 METRIC = "decode fp8-KV HBM GB/s (% of peak); prefill TFLOP/s (% of MFMA peak)"
-ELEM = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1}
+ELEM = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e4m3fnuz": 1, "e5m2fnuz": 1}
 
 
 def decode_bytes(w: dict) -> int:
@@ -232,12 +233,13 @@ def copy_bandwidth(mb: int = 512, steps: int = 20) -> float:
 
 
 def decode_extra(steps, warmup):
-    """Long-context split-KV decode and the three KV types of the mixed-dtype
-    decode workload: HIP-event medians and HBM rates (context beside the main
-    line; each is a separate decode workload)."""
+    """Long-context split-KV decode, the three KV types of the mixed-dtype
+    decode workload, and the batch-decode workload over an e4m3fnuz cache:
+    HIP-event medians and HBM rates (context beside the main line; each is a
+    separate decode workload)."""
     out = {}
     for key, cfg, kvd, copies in (("long_context", 4, None, 2), ("kv_f16", 5, "f16", 2), ("kv_bf16_mixed", 5, "bf16", 2),
-                                  ("kv_e4m3", 5, "e4m3", 4)):
+                                  ("kv_e4m3", 5, "e4m3", 4), ("kv_e4m3fnuz", 2, "e4m3fnuz", 4)):
         w, wall_ms, ev = run_decode_bench(steps, warmup, copies, cfg=cfg, kvd=kvd)
         nb = decode_bytes(w)
         med = float(np.median(ev))

@@ -86,8 +86,8 @@ typedef enum fi_dtype {
   FI_F32 = 5,          /* refused everywhere */
   FI_I8 = 6,           /* refused: no float interpretation ([C] design notes) */
   FI_U8 = 7,           /* refused, as int8 */
-  FI_F8_E4M3_FNUZ = 8, /* refused: the gfx942 variant, bias 8 */
-  FI_F8_E5M2_FNUZ = 9  /* refused: the gfx942 variant, bias 16 */
+  FI_F8_E4M3_FNUZ = 8, /* the gfx942 variant, bias 8 ([C] design notes): decode only */
+  FI_F8_E5M2_FNUZ = 9  /* the gfx942 variant, bias 16: decode only */
 } fi_dtype;
 
 typedef enum fi_status {
@@ -132,7 +132,8 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
 
 /* Batched decode: one query token per request against its paged K/V.
  *   q        [dev] [batch, num_qo_heads, head_dim], q_dtype in {FI_F16, FI_BF16}
- *   kv       the paged cache; KV dtype in {F16, BF16, E4M3, E5M2}.  A 2-byte KV
+ *   kv       the paged cache; KV dtype in {F16, BF16, E4M3, E5M2, E4M3_FNUZ,
+ *            E5M2_FNUZ} (fnuz: exact bit-level widening, decode only).  A 2-byte KV
  *            dtype may differ from q's ([C] design notes: mixed 2-byte decode
  *            is correct); the products then run in bf16 with every fp16
  *            value split exactly into two bf16 parts, so nothing is rounded
@@ -245,7 +246,10 @@ fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const
                            float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Widen n fp8 codes into a 2-byte type with the same device conversion the
- * attention kernels use (no scaling).  src in {E4M3, E5M2}, dst in {F16, BF16};
+ * attention kernels use (no scaling; the e4m3fnuz values, which the kernels
+ * hold as value * 2^-7 with 2^7 folded into their scales, are returned as the
+ * values themselves).  src in {E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ}, dst in
+ * {F16, BF16}; the fnuz NaN code 0x80 reads as -0;
  * codes [dev] [n] bytes, out [dev] [n] 2-byte values.  This makes the
  * conversion testable code by code ([C] design notes: the vec_cast paragraph
  * records a decoder with the wrong bias and broken denormals that no test

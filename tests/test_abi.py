@@ -152,8 +152,8 @@ DTYPE_REFUSALS = [
     ("decode", dict(k="i8"), 1, "KV cache has dtype int8, which has no float interpretation"),
     ("decode", dict(k="u8"), 1, "KV cache has dtype uint8, which has no float interpretation"),
     ("decode", dict(k="f32"), 1, "KV cache has dtype float32"),
-    ("decode", dict(k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant"),
-    ("decode", dict(k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
+    ("prefill", dict(k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant; fnuz caches are read by the decode"),
+    ("prefill", dict(k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
     ("prefill", dict(q="f16", k="bf16"), 1,
      "fi_batch_prefill_paged: q has dtype float16 but the KV cache has dtype bfloat16; prefill needs a 2-byte KV"),
     ("prefill", dict(q="bf16", k="f16"), 1, "q has dtype bfloat16 but the KV cache has dtype float16"),
@@ -221,6 +221,16 @@ def test_decode_accepts_mixed_2byte_before_pointer_checks(L):
         kv, keep = _kv(k)
         st = _decode(L, kv, q=q)
         assert st == 3 and "must not be NULL" in _err(L), _err(L)
+
+
+@no_gpu
+def test_decode_accepts_fnuz_before_pointer_checks(L):
+    """fnuz caches pass the decode dtype checks (the next refusal is the NULL
+    pointer), in the batch and the single call."""
+    for k in ("e4m3fnuz", "e5m2fnuz"):
+        kv, keep = _kv(k)
+        assert _decode(L, kv) == 3 and "must not be NULL" in _err(L), _err(L)
+        assert _single(L, k=k) == 3 and "must not be NULL" in _err(L), _err(L)
 
 
 @no_gpu
@@ -328,6 +338,7 @@ def test_workspace_too_small(L, monkeypatch):
 def test_widen_refusals(L):
     assert L.fi_fp8_widen(None, 4, fi.DTYPES["f16"], fi.DTYPES["f16"], None, None) == 1
     assert "src has dtype float16" in _err(L)
+    assert L.fi_fp8_widen(None, 4, fi.DTYPES["e4m3fnuz"], fi.DTYPES["f16"], None, None) == 3  # fnuz passes dtypes
     assert L.fi_fp8_widen(None, 4, fi.DTYPES["e4m3"], fi.DTYPES["e4m3"], None, None) == 1
     assert L.fi_fp8_widen(None, 4, fi.DTYPES["e4m3"], fi.DTYPES["bf16"], None, None) == 3
     assert L.fi_fp8_widen(None, 0, fi.DTYPES["e4m3"], fi.DTYPES["bf16"], None, None) == 0

@@ -5,7 +5,7 @@ Cases: every fp8 code widened bitwise; the measured configurations 1, 2, 4 and
 5 compared element by element at full size; a matrix of small shapes spanning
 several 32-token blocks, ragged tails, empty and one-token requests, page
 sizes 1..128, head_dim 64 and 128, GQA groups 1..32, all q / KV / o dtype
-combinations decode admits, forced split-KV; and the invariants: run-to-run
+combinations decode admits (fnuz caches included), forced split-KV; and the invariants: run-to-run
 bitwise determinism, bitwise page-permutation invariance, an fp8 run equal
 bitwise to a run on the same values pre-widened to q's type (the equivalence
 design of "fp8 KV cache in the in-tree prefill kernel", Test plan), the
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 
 # ------------------------------------------------------------------ fp8 codes
-@pytest.mark.parametrize("src", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("src", ["e4m3", "e5m2", "e4m3fnuz", "e5m2fnuz"])
 @pytest.mark.parametrize("dst", ["f16", "bf16"])
 def test_fp8_widen_all_codes_bitwise(gpu_device, src, dst):
     say("widen", src, dst)
@@ -36,7 +36,9 @@ def test_fp8_widen_all_codes_bitwise(gpu_device, src, dst):
     fi.fi_fp8_widen(codes, src, out)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
-    ref = fp8_table(src)[codes.cpu().numpy()]
+    ref = fp8_table(src)[codes.cpu().numpy()].copy()
+    if src.endswith("fnuz"):
+        ref[codes.cpu().numpy() == 0x80] = -0.0  # the fnuz NaN code reads as -0 (documented)
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], ref[~nan])
@@ -83,6 +85,11 @@ SMALL = [
     ("bf16", "f16", "f16", 16, 128, 32, 8, (600, 90), "128"),        # mixed 2-byte decode
     ("f16", "bf16", "bf16", 8, 128, 8, 8, (300, 12), None),          # mixed the other way
     ("e5m2", "f16", "f16", 2, 128, 16, 16, (55, 1, 0, 1024), "128"),
+    # fnuz caches (decode only)
+    ("e4m3fnuz", "f16", "f16", 16, 128, 32, 8, (1, 31, 32, 33, 200, 517, 0, 64), None),
+    ("e4m3fnuz", "bf16", "bf16", 16, 128, 32, 8, (700, 129, 5), "128"),
+    ("e5m2fnuz", "f16", "bf16", 64, 128, 64, 8, (1000, 3, 2049), "256"),
+    ("e5m2fnuz", "bf16", "f16", 4, 64, 8, 2, (77, 300, 1), None),
 ]
 
 
@@ -158,6 +165,43 @@ def test_config5_refusals_with_real_tensors(gpu_device):
     assert torch.all(o2 == 7.0)
 
 
+@pytest.mark.parametrize("kvd", ["e4m3fnuz", "e5m2fnuz"])
+def test_fnuz_batch_decode_shapes_and_single(gpu_device, kvd):
+    """The batch-decode shapes (64 requests of 512..4096 tokens, 32/8 heads,
+    page 16 shuffled) over an fnuz cache, whole requests against the oracle;
+    and fi_single_decode over one request's rows."""
+    say("fnuz config2 shapes", kvd)
+    w = make_config(2, kvd=kvd)
+    d = upload(w, gpu_device)
+    og, lg, _ = run_decode(w, d)
+    reqs = [0, 17, 40, 63]
+    o_ref, l_ref = OA.batch_decode(w, requests=reqs)
+    assert_parity(og[reqs], lg[reqs], o_ref[reqs], l_ref[reqs], "bf16", f"{kvd} batch decode")
+    i = 5
+    pages = w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
+    n = int(w["kv_lens"][i])
+    k = torch.from_numpy(np.ascontiguousarray(w["k_pool"][pages].reshape(-1, 8, 128)[:n])).to(gpu_device)
+    v = torch.from_numpy(np.ascontiguousarray(w["v_pool"][pages].reshape(-1, 8, 128)[:n])).to(gpu_device)
+    q1 = d["q"][i]
+    o1 = torch.empty_like(q1)
+    l1 = torch.empty(32, dtype=torch.float32, device=gpu_device)
+    fi.fi_single_decode(q1, k, v, o1, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=kvd, lse=l1)
+    torch.cuda.synchronize()
+    o_s, l_s = OA.single_decode(w["q"][i], "bf16", k.cpu().numpy(), v.cpu().numpy(), kvd, w["k_scale"], w["v_scale"])
+    assert_parity(o1.double().cpu().numpy(), l1.double().cpu().numpy(), o_s, l_s, "bf16", f"{kvd} single decode")
+
+
+def test_prefill_refuses_fnuz(gpu_device):
+    w = make_paged(8, qo_lens=[4], prefix_lens=[10], hq=8, hkv=2, d=64, page=16, q="f16", kvd="e4m3fnuz")
+    d = upload(w, gpu_device)
+    kv, keep = paged_kv(w, d)
+    o = torch.full((4, 8, 64), 7.0, dtype=torch.float16, device=gpu_device)
+    with pytest.raises(fi.FiValueError, match="fnuz caches are read by the decode calls only"):
+        fi.fi_batch_prefill_paged(d["q"], d["qo_indptr"], kv, o, qo_indptr_h=w["qo_indptr"])
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0)
+
+
 # ------------------------------------------------------------------ invariants
 def _mid_workload(seed=21, kvd="e4m3", q="bf16", extra_pages=0):
     return make_paged(seed, kv_lens=[1500, 33, 900, 2048, 7, 640], hq=32, hkv=8, d=128, page=16, q=q, kvd=kvd,
@@ -181,7 +225,7 @@ def test_determinism_and_page_permutation(gpu_device):
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
-@pytest.mark.parametrize("kvd,q", [("e4m3", "bf16"), ("e5m2", "f16")])
+@pytest.mark.parametrize("kvd,q", [("e4m3", "bf16"), ("e5m2", "f16"), ("e4m3fnuz", "f16"), ("e5m2fnuz", "bf16")])
 def test_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
     """fp8 K/V give bit-identical output to the same values stored widened in
     q's 2-byte type, with the same scales."""
