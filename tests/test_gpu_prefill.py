@@ -3,7 +3,7 @@ ABI, against the float64 oracle.
 
 Cases: the causal prefill configuration (3) at full size -- four requests
 compared element by element and sampled rows of every request; a matrix of
-small shapes (GQA groups 1, 2, 3, 4, 8; head_dim 64 and 128; page sizes 1 to
+small shapes (GQA groups 1, 2, 3, 4, 8, 32; head_dim 64 and 128; page sizes 1 to
 128; fp8 and same-type 2-byte KV; causal and non-causal; ragged query and
 prefix lengths that leave partial tiles); rows with no visible key; requests
 without queries or without keys; decode equal to prefill with one query per
@@ -34,6 +34,9 @@ SMALL = [
     ("bf16", "bf16", "bf16", 8, 64, 4, 2, (150,), (200,), True),
     ("e4m3", "bf16", "bf16", 128, 128, 32, 8, (70, 300), (400, 2), False),  # page 128, non-causal with prefix
     ("e5m2", "f16", "f16", 128, 64, 16, 4, (129, 64), (0, 190), True),
+    ("e4m3", "f16", "f16", 16, 128, 32, 1, (65, 3), (100, 0), True),       # group 32: 8 head subgroups
+    ("e5m2", "bf16", "bf16", 1, 64, 2, 2, (300,), (0,), True),             # page 1, one q head per kv head
+    ("e4m3", "f16", "f16", 16, 128, 8, 8, (700,), (1300,), False),         # long non-causal with a prefix
 ]
 
 
