@@ -42,6 +42,18 @@
 // separate sum of the fp32 values.
 // Each wave also overlaps its two phases: the QK MFMAs of the next tile are
 // issued between the exponentials of the current one.
+//
+// Variants (template flags):
+//   * RAGGED: K/V rows contiguous per request (row indptr[b] + t), the page
+//     walk reduced to an addition; with NULL index arrays a single request
+//     takes its lengths from the kernel arguments.
+//   * Q8 (an fp8 query, q_scale folded into the logit scale -- "Enable Hopper
+//     FA3 FP8 attention in decode.py", flashinfer PR #2148, review comments):
+//     K stays fp8 from HBM to the matrix cores (raw LDS tile) and S^T = K Q^T
+//     runs on v_mfma_f32_32x32x64_f8f6f4, twice the 16-bit rate; P V stays fp16.
+//   * P8 (with Q8): V stays fp8 too, the probabilities are rounded to e4m3
+//     in registers and P V runs on the same fp8 MFMA; the output is
+//     normalised by the fp32 sum of the unrounded probabilities.
 #include <type_traits>
 
 #include "fi_device.hpp"
