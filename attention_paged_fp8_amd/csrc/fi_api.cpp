@@ -93,8 +93,8 @@ fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_d
 
 // Checks 1-5 for a call that takes an fp8 query: q in {e4m3, e5m2}; o given
 // explicitly as a 2-byte type (the default, q's dtype, would be fp8); k == v;
-// an fp8 KV cache.
-fi_status check_dtypes_fp8q(const char* fn, fi_dtype q, fi_dtype o, fi_dtype k, fi_dtype v) {
+// an fp8 KV cache (fnuz too where `fnuz` is set: decode).
+fi_status check_dtypes_fp8q(const char* fn, fi_dtype q, fi_dtype o, fi_dtype k, fi_dtype v, bool fnuz = false) {
   if (!is_ocp_fp8(q))
     return fail(FI_E_DTYPE, fn, "q has dtype %s; this call takes an fp8 query (float8_e4m3fn or float8_e5m2)",
                 dtype_name(q));
@@ -109,10 +109,10 @@ fi_status check_dtypes_fp8q(const char* fn, fi_dtype q, fi_dtype o, fi_dtype k, 
   if (k == FI_I8 || k == FI_U8)
     return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be "
                 "float8_e4m3fn or float8_e5m2", dtype_name(k));
-  if (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ)
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; this library decodes OCP "
-                "float8_e4m3fn / float8_e5m2", dtype_name(k));
-  if (!is_ocp_fp8(k))
+  if (!fnuz && (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ))
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; fnuz caches are read by the "
+                "decode calls only", dtype_name(k));
+  if (!is_any_fp8(k))
     return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; an fp8 query needs an fp8 KV cache "
                 "(float8_e4m3fn or float8_e5m2)", dtype_name(q), dtype_name(k));
   return FI_OK;
@@ -462,13 +462,11 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
   return partial_bytes(batch, max_chunks, num_qo_heads, head_dim) + (size_t)batch * num_qo_heads * 4;
 }
 
-fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
-                                const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  static const char* fn = "fi_batch_decode_paged";
-  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
-  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, false);
-  if (st != FI_OK) return st;
+// Batched paged decode after the dtype checks (q_scale: 1 for a 2-byte query).
+static fi_status decode_paged(const char* fn, const void* q, fi_dtype q_dtype, float q_scale, int32_t batch,
+                              int32_t num_qo_heads, const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse,
+                              float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  fi_status st;
   if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is outside [0, 2^31)", batch);
   if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
   if (batch > 0) {
@@ -497,9 +495,34 @@ fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, 
   p.num_qo_heads = num_qo_heads;
   p.num_kv_heads = kv->num_kv_heads;
   p.group = num_qo_heads / kv->num_kv_heads;
+  // q_scale joins k_scale in the logit scale (both multiply the fp32 products)
   return run_decode(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, kv->head_dim, kv->indptr_h, kv->last_page_len_h,
-                    kv->page_size, max_kv, total_kv, workspace, workspace_bytes, sm_scale, kv->k_scale, kv->v_scale,
-                    reinterpret_cast<hipStream_t>(stream));
+                    kv->page_size, max_kv, total_kv, workspace, workspace_bytes, sm_scale, kv->k_scale * q_scale,
+                    kv->v_scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
+                                const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "fi_batch_decode_paged";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, false);
+  if (st != FI_OK) return st;
+  return decode_paged(fn, q, q_dtype, 1.0f, batch, num_qo_heads, kv, o, o_dtype, lse, sm_scale, workspace,
+                      workspace_bytes, stream);
+}
+
+fi_status fi_batch_decode_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, int32_t batch,
+                                     int32_t num_qo_heads, const fi_paged_kv* kv, void* o, fi_dtype o_dtype,
+                                     float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  static const char* fn = "fi_batch_decode_paged_fp8q";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes_fp8q(fn, q_dtype, o_dtype, kv->k_dtype, kv->v_dtype, true);
+  if (st != FI_OK) return st;
+  if (!std::isfinite(q_scale) || !(q_scale > 0.f)) return fail(FI_E_ARG, fn, "q_scale=%g must be finite and > 0", q_scale);
+  return decode_paged(fn, q, q_dtype, q_scale, batch, num_qo_heads, kv, o, o_dtype, lse, sm_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const void* v, fi_dtype k_dtype,

@@ -82,7 +82,10 @@ __device__ __forceinline__ int request_kv_len(const DecodeParams& p, int b) {
   return (e > a) ? (e - a - 1) * p.page_size + p.last_page_len[b] : 0;
 }
 
-template <bool QBF16, int KVF, bool OBF16, int D>
+// Q8: an fp8 query (FMT_E4M3 / FMT_E5M2 codes, q_scale folded into the logit
+// scale by the host), widened exactly to fp16 as it is loaded; QBF16 is then
+// false and the kernel runs its fp16 path.
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8 = 0>
 __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(const DecodeParams p) {
   using Cfg = DecodeCfg<QBF16, KVF, OBF16, D>;
   constexpr bool MB = Cfg::MBF16;
@@ -122,7 +125,15 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
     // Q^T operand: lane (qg, c) holds q[row c][DL*qg + 8s + j], j = 0..7.
     uint4 qop[Cfg::NS];
     uint4 qlo[Cfg::kSplitQ ? Cfg::NS : 1];
-    {
+    if constexpr (Q8 != 0) {
+      const uint2* qp = reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(p.q) +
+                                                       ((int64_t)b * p.num_qo_heads + h) * D + Cfg::DL * qg);
+#pragma unroll
+      for (int s = 0; s < Cfg::NS; ++s) {
+        const uint2 raw = row_ok ? qp[s] : make_uint2(0, 0);
+        qop[s] = widen8<false, Q8>(raw.x, raw.y);
+      }
+    } else {
       const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
                                                        ((int64_t)b * p.num_qo_heads + h) * D + Cfg::DL * qg);
 #pragma unroll
@@ -528,63 +539,74 @@ __global__ __launch_bounds__(256) void widen_kernel(const uint8_t* codes, int64_
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <bool QBF16, int KVF, bool OBF16, int D>
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8>
 static hipError_t launch_decode_t(const DecodeParams& p, int batch, hipStream_t s) {
   dim3 grid(p.balanced ? (unsigned)p.n_wg : (unsigned)p.max_chunks * p.n_hgroups * p.n_sgroups * batch);
   if (grid.x == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<QBF16, KVF, OBF16, D>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<QBF16, KVF, OBF16, D, Q8>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool QBF16, int KVF, bool OBF16>
+template <bool QBF16, int KVF, bool OBF16, int Q8>
 static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, int batch, hipStream_t s) {
-  if (head_dim == 128) return launch_decode_t<QBF16, KVF, OBF16, 128>(p, batch, s);
-  return launch_decode_t<QBF16, KVF, OBF16, 64>(p, batch, s);
+  if (head_dim == 128) return launch_decode_t<QBF16, KVF, OBF16, 128, Q8>(p, batch, s);
+  return launch_decode_t<QBF16, KVF, OBF16, 64, Q8>(p, batch, s);
 }
 
-template <bool QBF16, int KVF>
+template <bool QBF16, int KVF, int Q8>
 static hipError_t launch_decode_o(const DecodeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {
-  if (o_fmt == FMT_BF16) return launch_decode_d<QBF16, KVF, true>(p, head_dim, batch, s);
-  return launch_decode_d<QBF16, KVF, false>(p, head_dim, batch, s);
+  if (o_fmt == FMT_BF16) return launch_decode_d<QBF16, KVF, true, Q8>(p, head_dim, batch, s);
+  return launch_decode_d<QBF16, KVF, false, Q8>(p, head_dim, batch, s);
 }
 
-template <bool QBF16>
+template <bool QBF16, int Q8>
 static hipError_t launch_decode_kv(const DecodeParams& p, int kv_fmt, int o_fmt, int head_dim, int batch,
                                    hipStream_t s) {
   switch (kv_fmt) {
-    case FMT_F16: return launch_decode_o<QBF16, FMT_F16>(p, o_fmt, head_dim, batch, s);
-    case FMT_BF16: return launch_decode_o<QBF16, FMT_BF16>(p, o_fmt, head_dim, batch, s);
-    case FMT_E4M3: return launch_decode_o<QBF16, FMT_E4M3>(p, o_fmt, head_dim, batch, s);
-    case FMT_E4M3_FNUZ: return launch_decode_o<QBF16, FMT_E4M3_FNUZ>(p, o_fmt, head_dim, batch, s);
-    case FMT_E5M2_FNUZ: return launch_decode_o<QBF16, FMT_E5M2_FNUZ>(p, o_fmt, head_dim, batch, s);
-    default: return launch_decode_o<QBF16, FMT_E5M2>(p, o_fmt, head_dim, batch, s);
+    case FMT_E4M3: return launch_decode_o<QBF16, FMT_E4M3, Q8>(p, o_fmt, head_dim, batch, s);
+    case FMT_E5M2: return launch_decode_o<QBF16, FMT_E5M2, Q8>(p, o_fmt, head_dim, batch, s);
+    case FMT_E4M3_FNUZ: return launch_decode_o<QBF16, FMT_E4M3_FNUZ, Q8>(p, o_fmt, head_dim, batch, s);
+    case FMT_E5M2_FNUZ: return launch_decode_o<QBF16, FMT_E5M2_FNUZ, Q8>(p, o_fmt, head_dim, batch, s);
+  }
+  if constexpr (Q8 != 0) {
+    return hipErrorInvalidValue;  // an fp8 query needs an fp8 cache
+  } else {
+    if (kv_fmt == FMT_F16) return launch_decode_o<QBF16, FMT_F16, 0>(p, o_fmt, head_dim, batch, s);
+    return launch_decode_o<QBF16, FMT_BF16, 0>(p, o_fmt, head_dim, batch, s);
   }
 }
 
-template <bool QBF16, int KVF, bool OBF16, int D>
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8>
 static int occupancy_t() {
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&decode_kernel<QBF16, KVF, OBF16, D>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&decode_kernel<QBF16, KVF, OBF16, D, Q8>),
                                                    256, 0) != hipSuccess)
     return 0;
   return occ;
 }
 
-template <bool QBF16, int KVF, bool OBF16>
-static int occupancy_d(int d) { return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128>() : occupancy_t<QBF16, KVF, OBF16, 64>(); }
+template <bool QBF16, int KVF, bool OBF16, int Q8>
+static int occupancy_d(int d) {
+  return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128, Q8>() : occupancy_t<QBF16, KVF, OBF16, 64, Q8>();
+}
 
-template <bool QBF16, int KVF>
-static int occupancy_o(int o, int d) { return o == FMT_BF16 ? occupancy_d<QBF16, KVF, true>(d) : occupancy_d<QBF16, KVF, false>(d); }
+template <bool QBF16, int KVF, int Q8>
+static int occupancy_o(int o, int d) {
+  return o == FMT_BF16 ? occupancy_d<QBF16, KVF, true, Q8>(d) : occupancy_d<QBF16, KVF, false, Q8>(d);
+}
 
-template <bool QBF16>
+template <bool QBF16, int Q8>
 static int occupancy_kv(int kv, int o, int d) {
   switch (kv) {
-    case FMT_F16: return occupancy_o<QBF16, FMT_F16>(o, d);
-    case FMT_BF16: return occupancy_o<QBF16, FMT_BF16>(o, d);
-    case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3>(o, d);
-    case FMT_E4M3_FNUZ: return occupancy_o<QBF16, FMT_E4M3_FNUZ>(o, d);
-    case FMT_E5M2_FNUZ: return occupancy_o<QBF16, FMT_E5M2_FNUZ>(o, d);
-    default: return occupancy_o<QBF16, FMT_E5M2>(o, d);
+    case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3, Q8>(o, d);
+    case FMT_E5M2: return occupancy_o<QBF16, FMT_E5M2, Q8>(o, d);
+    case FMT_E4M3_FNUZ: return occupancy_o<QBF16, FMT_E4M3_FNUZ, Q8>(o, d);
+    case FMT_E5M2_FNUZ: return occupancy_o<QBF16, FMT_E5M2_FNUZ, Q8>(o, d);
+  }
+  if constexpr (Q8 != 0) {
+    return 0;
+  } else {
+    return kv == FMT_F16 ? occupancy_o<QBF16, FMT_F16, 0>(o, d) : occupancy_o<QBF16, FMT_BF16, 0>(o, d);
   }
 }
 
@@ -601,16 +623,19 @@ int device_cus() {
 
 int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
   // cached per (device, instantiation): the values cannot change while the process runs
-  static std::atomic<int> cache[64][2][10][2][2];
+  static std::atomic<int> cache[64][4][10][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || kv_fmt < 0 || kv_fmt >= 10) return 0;
-  std::atomic<int>& slot = cache[dev][q_fmt == FMT_BF16][kv_fmt][o_fmt == FMT_BF16][head_dim == 128];
+  const int qi = q_fmt == FMT_BF16 ? 1 : q_fmt == FMT_E4M3 ? 2 : q_fmt == FMT_E5M2 ? 3 : 0;
+  std::atomic<int>& slot = cache[dev][qi][kv_fmt][o_fmt == FMT_BF16][head_dim == 128];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int occ = q_fmt == FMT_BF16 ? occupancy_kv<true>(kv_fmt, o_fmt, head_dim)
-                                     : occupancy_kv<false>(kv_fmt, o_fmt, head_dim);
+  const int occ = qi == 1   ? occupancy_kv<true, 0>(kv_fmt, o_fmt, head_dim)
+                  : qi == 2 ? occupancy_kv<false, FMT_E4M3>(kv_fmt, o_fmt, head_dim)
+                  : qi == 3 ? occupancy_kv<false, FMT_E5M2>(kv_fmt, o_fmt, head_dim)
+                            : occupancy_kv<false, 0>(kv_fmt, o_fmt, head_dim);
   v = cus * occ;
   slot.store(v, std::memory_order_relaxed);
   return v;
@@ -618,8 +643,10 @@ int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
 
 hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                          hipStream_t s) {
-  if (q_fmt == FMT_BF16) return launch_decode_kv<true>(p, kv_fmt, o_fmt, head_dim, batch, s);
-  return launch_decode_kv<false>(p, kv_fmt, o_fmt, head_dim, batch, s);
+  if (q_fmt == FMT_BF16) return launch_decode_kv<true, 0>(p, kv_fmt, o_fmt, head_dim, batch, s);
+  if (q_fmt == FMT_E4M3) return launch_decode_kv<false, FMT_E4M3>(p, kv_fmt, o_fmt, head_dim, batch, s);
+  if (q_fmt == FMT_E5M2) return launch_decode_kv<false, FMT_E5M2>(p, kv_fmt, o_fmt, head_dim, batch, s);
+  return launch_decode_kv<false, 0>(p, kv_fmt, o_fmt, head_dim, batch, s);
 }
 
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {

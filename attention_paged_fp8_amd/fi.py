@@ -34,7 +34,8 @@ TORCH_DTYPES = {
 STATUS = {0: "FI_OK", 1: "FI_E_DTYPE", 2: "FI_E_SHAPE", 3: "FI_E_ARG", 4: "FI_E_WORKSPACE", 5: "FI_E_HIP"}
 
 # every symbol include/fi.h declares
-EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_prefill_paged",
+EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_decode_paged_fp8q",
+           "fi_batch_prefill_paged",
            "fi_batch_prefill_paged_fp8q", "fi_batch_prefill_ragged", "fi_single_prefill", "fi_single_decode", "fi_fp8_widen")
 
 
@@ -97,6 +98,9 @@ def lib() -> ctypes.CDLL:
     L.fi_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.fi_batch_decode_paged.restype = en
     L.fi_batch_decode_paged.argtypes = [vp, en, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz, vp]
+    L.fi_batch_decode_paged_fp8q.restype = en
+    L.fi_batch_decode_paged_fp8q.argtypes = [vp, en, f32, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz,
+                                             vp]
     L.fi_batch_prefill_paged.restype = en
     L.fi_batch_prefill_paged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(PagedKV), i32, vp, en, vp, f32, vp,
                                          sz, vp]
@@ -197,6 +201,21 @@ def fi_batch_decode_paged(q, kv: PagedKV, o, *, q_dtype=None, o_dtype=None, lse=
         int(batch if batch is not None else q.shape[0]), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
         ctypes.byref(kv), _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale),
         _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def fi_batch_decode_paged_fp8q(q, kv: PagedKV, o, *, q_dtype, o_dtype=None, q_scale=1.0, lse=None, sm_scale=0.0,
+                               workspace=None, workspace_bytes=None, batch=None, num_qo_heads=None, stream=None):
+    """q [batch, H_qo, D] fp8 codes (a float8 tensor, or uint8 with q_dtype naming
+    the format); o [batch, H_qo, D] float16 or bfloat16."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    st = lib().fi_batch_decode_paged_fp8q(
+        _ptr(q), _dt(q_dtype), float(q_scale), int(batch if batch is not None else q.shape[0]),
+        int(num_qo_heads if num_qo_heads is not None else q.shape[1]), ctypes.byref(kv), _ptr(o),
+        _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale), _ptr(workspace),
+        int(workspace_bytes), _stream(stream, q, o))
     check(st)
     return o
 

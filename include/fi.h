@@ -152,6 +152,22 @@ fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, 
                                 const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Batched decode with an fp8 query ([A]: fp8 attention in decode.py; review
+ * comments: q_scale folded into sm_scale for the first product).
+ *   q        [dev] [batch, num_qo_heads, head_dim] fp8 codes, q_dtype in
+ *            {FI_F8_E4M3, FI_F8_E5M2}; real q = code * q_scale
+ *   q_scale  per-tensor, finite and > 0
+ *   kv       an fp8 cache: E4M3, E5M2, E4M3_FNUZ or E5M2_FNUZ
+ *   o_dtype  FI_F16 or FI_BF16, given explicitly
+ * Other arguments, the split-KV workspace and results as
+ * fi_batch_decode_paged.  The codes are widened exactly to fp16 as they are
+ * loaded and the products run as with an fp16 query, so the result matches
+ * fi_batch_decode_paged on the widened values (with sm_scale * q_scale). */
+fi_status fi_batch_decode_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, int32_t batch,
+                                     int32_t num_qo_heads, const fi_paged_kv* kv, void* o, fi_dtype o_dtype,
+                                     float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Batched prefill over the paged cache ([C] Summary and Refusals).
  *   q          [dev] [qo_indptr[batch], num_qo_heads, head_dim]
  *   qo_indptr  [dev] [batch+1] query ranges; qo_indptr_h its [host] copy.

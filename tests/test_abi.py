@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -309,6 +309,28 @@ def test_ragged_and_single_prefill_refusals(L):
     assert _single_prefill(L, qo_len=0, kv_len=0) == 0
     kv, keep = _ragged(ptrs=True)
     assert L.fi_batch_prefill_ragged(None, 1, None, None, 0, 4, ctypes.byref(kv), 1, None, 0, None, 0.0, None) == 0
+
+
+def _decode_fp8q(L, kv, q="e4m3", o="f16", hq=4, batch=2, qp=None, op=None, q_scale=1.0):
+    return L.fi_batch_decode_paged_fp8q(qp, fi.DTYPES[q], q_scale, batch, hq, ctypes.byref(kv), op, fi.DTYPES[o], None,
+                                        0.0, None, 0, None)
+
+
+@no_gpu
+def test_decode_fp8q_refusals(L):
+    kv, keep = _kv("e4m3")
+    assert _decode_fp8q(L, kv, q="bf16") == 1 and "fi_batch_decode_paged_fp8q: q has dtype bfloat16" in _err(L)
+    assert _decode_fp8q(L, kv, o="default") == 1 and "o_dtype must be given for an fp8 query" in _err(L)
+    assert _decode_fp8q(L, kv, o="e4m3") == 1 and "an fp8 output is not supported" in _err(L)
+    kv2, keep2 = _kv("f16")
+    assert _decode_fp8q(L, kv2) == 1 and "an fp8 query needs an fp8 KV cache" in _err(L)
+    kv3, keep3 = _kv("e4m3", "e5m2")
+    assert _decode_fp8q(L, kv3) == 1 and "k has dtype float8_e4m3fn but v has dtype float8_e5m2" in _err(L)
+    kv4, keep4 = _kv("e5m2fnuz")  # fnuz passes the dtype checks in decode
+    assert _decode_fp8q(L, kv4) == 3 and "must not be NULL" in _err(L)
+    assert _decode_fp8q(L, kv, qp=0x10000, op=0x10000, q_scale=-1.0) == 3 and "q_scale=-1" in _err(L)
+    kv5, keep5 = _kv("e4m3", d=48)
+    assert _decode_fp8q(L, kv5) == 2 and "head_dim=48" in _err(L)
 
 
 @no_gpu

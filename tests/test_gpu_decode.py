@@ -20,7 +20,7 @@ import oracle.attention as OA
 from oracle.fp8 import fp8_table
 from attention_paged_fp8_amd import fi
 from workloads import make_config, make_paged
-from gpu_util import (O_TOL, T2, assert_parity, dev_2byte, paged_kv, run_decode, say, upload)
+from gpu_util import (O_TOL, T2, assert_parity, dev_2byte, paged_kv, run_decode, say, upload, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +189,60 @@ def test_fnuz_batch_decode_shapes_and_single(gpu_device, kvd):
     torch.cuda.synchronize()
     o_s, l_s = OA.single_decode(w["q"][i], "bf16", k.cpu().numpy(), v.cpu().numpy(), kvd, w["k_scale"], w["v_scale"])
     assert_parity(o1.double().cpu().numpy(), l1.double().cpu().numpy(), o_s, l_s, "bf16", f"{kvd} single decode")
+
+
+def run_decode_fp8q(w: dict, d: dict, *, split=None, workspace=True):
+    import os
+    B = len(w["kv_lens"])
+    o = torch.full((B, w["num_qo_heads"], w["head_dim"]), float("nan"), dtype=T2[w["o_dtype"]], device=gpu_dev(d))
+    lse = torch.full((B, w["num_qo_heads"]), float("nan"), dtype=torch.float32, device=gpu_dev(d))
+    ws = workspace_for(w, gpu_dev(d)) if workspace else None
+    kv, keep = paged_kv(w, d)
+    old = os.environ.get("FI_SPLIT_KV")
+    try:
+        if split is not None:
+            os.environ["FI_SPLIT_KV"] = str(split)
+        fi.fi_batch_decode_paged_fp8q(d["q"], kv, o, q_dtype=w["q_dtype"], q_scale=w["q_scale"], lse=lse, workspace=ws)
+    finally:
+        if split is not None:
+            if old is None:
+                os.environ.pop("FI_SPLIT_KV", None)
+            else:
+                os.environ["FI_SPLIT_KV"] = old
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def gpu_dev(d):
+    return d["q"].device
+
+
+FP8Q = [
+    # (q, kvd, o, page, d, hq, hkv, lens, split)
+    ("e4m3", "e4m3", "bf16", 16, 128, 32, 8, (1, 31, 32, 33, 200, 517, 0, 64), None),
+    ("e5m2", "e4m3fnuz", "f16", 16, 128, 32, 8, (700, 129, 5), "128"),
+    ("e4m3", "e5m2", "f16", 4, 64, 8, 2, (77, 300, 1), None),
+    ("e5m2", "e5m2fnuz", "bf16", 64, 128, 64, 8, (1000, 3, 2049), "256"),
+]
+
+
+@pytest.mark.parametrize("case", FP8Q, ids=[f"q{c[0]}-{c[1]}-o{c[2]}-p{c[3]}-d{c[4]}-h{c[5]}x{c[6]}-s{c[8]}" for c in FP8Q])
+def test_decode_fp8_query(gpu_device, case):
+    """An fp8 query with its q_scale (fi_batch_decode_paged_fp8q) against the
+    oracle, and against fi_batch_decode_paged on the same values widened to
+    fp16 with q_scale moved into sm_scale."""
+    q, kvd, o, page, d_, hq, hkv, lens, split = case
+    say("decode fp8 query", case)
+    w = make_paged(12, kv_lens=list(lens), hq=hq, hkv=hkv, d=d_, page=page, q=q, kvd=kvd, o=o, extra_pages=2)
+    dv = upload(w, gpu_device)
+    og, lg = run_decode_fp8q(w, dv, split=split)
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(og, lg, o_ref, l_ref, o, str(case))
+    qw = fp8_table(q)[w["q"]].astype(np.float32)
+    w16 = dict(w, q=None, q_dtype="f16", q_scale=1.0)
+    d16 = dict(dv, q=torch.from_numpy(qw).to(torch.float16).to(gpu_device))
+    o2, l2, _ = run_decode(w16, d16, split=split, sm_scale=OA.default_sm_scale(d_) * w["q_scale"])
+    assert np.max(np.abs(og - o2)) <= O_TOL[o] and np.max(np.abs(lg[np.isfinite(lg)] - l2[np.isfinite(l2)])) <= 1e-3
 
 
 def test_prefill_refuses_fnuz(gpu_device):
