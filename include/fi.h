@@ -2,7 +2,9 @@
  * fi.h -- C ABI of a gfx950 (MI355X) library for batched attention over a
  * paged KV cache, decode and causal prefill, with fp16/bf16 queries and
  * outputs and K/V stored as OCP fp8 (e4m3 or e5m2) with per-tensor scales,
- * widened to the query's 2-byte type as they are loaded.
+ * widened to the query's 2-byte type as they are loaded.  Beside these: fp8
+ * queries with a per-tensor q_scale (the *_fp8q calls), fnuz fp8 caches in
+ * decode, and prefill over ragged (non-paged) K/V or a single request.
  *
  * The problem statement these calls follow comes from three pages:
  *   [A] "Enable Hopper FA3 FP8 attention in decode.py" (flashinfer PR #2148):
@@ -65,7 +67,10 @@
  *   "fi_batch_decode_paged: k has dtype float16 but v has dtype bfloat16".
  * Checks run in a fixed order: query dtype, output dtype, k/v dtype match,
  * KV dtype, (prefill) 2-byte KV equal to q, then shapes, pointers, alignment,
- * page table and scales, then workspace.
+ * page table and scales, then workspace.  The fp8-query calls check in the
+ * same order with their own rules: q in {E4M3, E5M2}, o_dtype given
+ * explicitly as F16 or BF16, k == v, an fp8 cache (fnuz in decode only),
+ * then q_scale with the other scales.
  */
 #ifndef FI_H_
 #define FI_H_
