@@ -1,0 +1,136 @@
+"""Decode and prefill calls captured into a HIP graph and replayed.
+
+A serving loop replays a captured decode (or prefill) step instead of paying
+the host's launch cost per call.  Everything a call needs is planned on the
+host and travels in the kernel arguments, so a captured call replays the same
+work on whatever the buffers hold at replay time.  Each test captures the
+calls once, then replays the graph several times with eager work between the
+replays (a new query written into the captured buffer, an eager call on other
+buffers, synchronizations) and checks every replay bitwise against an eager
+call on the same inputs, and against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+from attention_paged_fp8_amd import fi
+from workloads import make_config
+from gpu_util import T2, assert_parity, paged_kv, say, upload, workspace_for
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _queries(w, n, device):
+    """n seeded query tensors of the workload's shape and dtype (the first is
+    the workload's own)."""
+    rng = np.random.default_rng(1234)
+    out = []
+    for i in range(n):
+        if i == 0:
+            bits = w["q"]
+        else:
+            x = rng.standard_normal(w["q"].shape).astype(np.float32)
+            bits = torch.from_numpy(x).to(T2[w["q_dtype"]]).view(torch.int16).numpy()
+        out.append(torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(T2[w["q_dtype"]]).to(device))
+    return out
+
+
+def _capture(fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream, capture_error_mode="thread_local"):
+        fn(stream)
+    return g
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_decode_graph_replays(gpu_device, cfg):
+    say("graph decode config", cfg)
+    w = make_config(cfg)
+    d = upload(w, gpu_device)
+    kv, keep = paged_kv(w, d)
+    B, H, D = len(w["kv_lens"]), w["num_qo_heads"], w["head_dim"]
+    ws = workspace_for(w, gpu_device)
+    q_in = torch.empty_like(d["q"])
+    o = torch.empty((B, H, D), dtype=T2[w["o_dtype"]], device=gpu_device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=gpu_device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    q_in.copy_(d["q"])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):  # warm the library's per-device caches outside the capture
+        fi.fi_batch_decode_paged(q_in, kv, o, lse=lse, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    g = _capture(lambda st: fi.fi_batch_decode_paged(q_in, kv, o, lse=lse, workspace=ws, stream=st), side)
+    torch.cuda.synchronize()
+
+    qs = _queries(w, REPLAYS, gpu_device)
+    ws_e = workspace_for(w, gpu_device)
+    for r in range(REPLAYS):
+        q_in.copy_(qs[r])  # eager work between replays
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_e = torch.full_like(o, float("nan"))
+        l_e = torch.full_like(lse, float("nan"))
+        fi.fi_batch_decode_paged(qs[r], kv, o_e, lse=l_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {r}: output differs from eager"
+        assert torch.equal(lse, l_e), f"replay {r}: lse differs from eager"
+        if r == 0 and cfg == 2:  # the long-context workload's full oracle is covered by the decode tests
+            o_ref, l_ref = OA.batch_decode(w)
+            assert_parity(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, w["o_dtype"],
+                          f"graph replay, config {cfg}")
+    del g
+
+
+def test_prefill_graph_replays(gpu_device):
+    say("graph prefill config 3")
+    w = make_config(3)
+    d = upload(w, gpu_device)
+    kv, keep = paged_kv(w, d)
+    T, H, D = int(w["qo_indptr"][-1]), w["num_qo_heads"], w["head_dim"]
+    q_in = torch.empty_like(d["q"])
+    o = torch.empty((T, H, D), dtype=T2[w["o_dtype"]], device=gpu_device)
+    lse = torch.empty((T, H), dtype=torch.float32, device=gpu_device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    q_in.copy_(d["q"])
+    torch.cuda.synchronize()
+
+    def call(st, q=q_in, out=o, l=lse):
+        fi.fi_batch_prefill_paged(q, d["qo_indptr"], kv, out, causal=True, lse=l, qo_indptr_h=w["qo_indptr"],
+                                  stream=st)
+
+    with torch.cuda.stream(side):
+        call(side)
+    torch.cuda.synchronize()
+    g = _capture(call, side)
+    torch.cuda.synchronize()
+
+    qs = _queries(w, REPLAYS, gpu_device)
+    for r in range(REPLAYS):
+        q_in.copy_(qs[r])
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_e = torch.full_like(o, float("nan"))
+        l_e = torch.full_like(lse, float("nan"))
+        call(torch.cuda.current_stream(), q=qs[r], out=o_e, l=l_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {r}: output differs from eager"
+        assert torch.equal(lse, l_e), f"replay {r}: lse differs from eager"
+        if r == 0:
+            rng = np.random.default_rng(7)  # sampled (token, head) outputs of the oracle, one by one
+            toks = rng.integers(0, T, 64)
+            heads = rng.integers(0, H, 64)
+            o_s, l_s = OA.attention_rows(w, toks, heads, causal=True)
+            o_np, l_np = o.double().cpu().numpy(), lse.double().cpu().numpy()
+            assert_parity(o_np[toks, heads], l_np[toks, heads], o_s, l_s, w["o_dtype"], "graph replay, prefill rows")
+    del g
