@@ -57,6 +57,12 @@
  *    stream has run the call.  The library allocates no memory and keeps no
  *    state between calls.  Host arrays must hold the same values as their
  *    device twins.
+ *  - A call issues kernel launches only (no memory set or copy): the plan it
+ *    derives from the host arrays travels in the kernel arguments, so a call
+ *    made while `stream` is being captured into a HIP graph records its
+ *    kernels, and each replay repeats the same plan on whatever the buffers
+ *    then hold.  The host arrays are not read again at replay; a changed
+ *    page table or batch needs a new capture.
  *
  * Errors
  * ------
