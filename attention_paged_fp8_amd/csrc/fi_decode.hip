@@ -86,7 +86,10 @@ __device__ __forceinline__ int request_kv_len(const DecodeParams& p, int b) {
 // scale by the host), widened exactly to fp16 as it is loaded; QBF16 is then
 // false and the kernel runs its fp16 path.
 template <bool QBF16, int KVF, bool OBF16, int D, int Q8 = 0>
-__global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(const DecodeParams p) {
+// (the e4m3fnuz form holds a step's codes in registers before widening them,
+// and is given the registers of two workgroups per CU)
+__global__ __launch_bounds__(256, KVF == FMT_E4M3_FNUZ ? 2 : FI_DECODE_MIN_WG_PER_CU) void decode_kernel(
+    const DecodeParams p) {
   using Cfg = DecodeCfg<QBF16, KVF, OBF16, D>;
   constexpr bool MB = Cfg::MBF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
@@ -220,18 +223,24 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
       }
     }
 
-    auto compute = [&](int st, const uint8_t* stage) {
+    // One step: kget(u) gives the u-th 16 bytes of this lane's K row, vget(i)
+    // the i-th transposed V read, w4 widens 4 fp8 codes.
+    auto compute_with = [&](int st, const uint8_t* stage, auto kget, auto vget, auto w4) {
+      auto w8 = [&](uint32_t lo, uint32_t hi) {
+        const uint2 a = w4(lo), b = w4(hi);
+        return make_uint4(a.x, a.y, b.x, b.y);
+      };
       const int tb = t_begin + st * kDecodeStep;
       // S^T = K Q^T over the step's 16 tokens
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < Cfg::DL * Cfg::KVB / 16; ++u) {
-        const uint4 x = *reinterpret_cast<const uint4*>(stage + k_off + 16 * ((kcol0 + u) ^ (c & swz)));
+        const uint4 x = kget(u);
         if constexpr (Cfg::kFp8) {
-          s = mfma16x16x32<MB>(widen8<MB, KVF>(x.x, x.y), qop[2 * u], s);
-          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(widen8<MB, KVF>(x.x, x.y), qlo[2 * u], s);
-          s = mfma16x16x32<MB>(widen8<MB, KVF>(x.z, x.w), qop[2 * u + 1], s);
-          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(widen8<MB, KVF>(x.z, x.w), qlo[2 * u + 1], s);
+          s = mfma16x16x32<MB>(w8(x.x, x.y), qop[2 * u], s);
+          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(w8(x.x, x.y), qlo[2 * u], s);
+          s = mfma16x16x32<MB>(w8(x.z, x.w), qop[2 * u + 1], s);
+          if constexpr (Cfg::kSplitQ) s = mfma16x16x32<true>(w8(x.z, x.w), qlo[2 * u + 1], s);
         } else if constexpr (Cfg::kSplitKV) {
           uint4 khi, klo;
           split_f16x8(x, khi, klo);
@@ -270,9 +279,9 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
       if constexpr (Cfg::kFp8) {
 #pragma unroll
         for (int i = 0; i < Cfg::NDB / 2; ++i) {
-          const uint2 v = lds_tr8(stage + v_off[i]);
-          acc[2 * i] = mfma16x16x16<MB>(widen4<MB, KVF>(v.x), pop, acc[2 * i]);
-          acc[2 * i + 1] = mfma16x16x16<MB>(widen4<MB, KVF>(v.y), pop, acc[2 * i + 1]);
+          const uint2 v = vget(i);
+          acc[2 * i] = mfma16x16x16<MB>(w4(v.x), pop, acc[2 * i]);
+          acc[2 * i + 1] = mfma16x16x16<MB>(w4(v.y), pop, acc[2 * i + 1]);
         }
       } else {
 #pragma unroll
@@ -288,6 +297,41 @@ __global__ __launch_bounds__(256, FI_DECODE_MIN_WG_PER_CU) void decode_kernel(co
             acc[i] = mfma16x16x16<MB>(v, pop, acc[i]);
           }
         }
+      }
+    };
+
+    auto k_lds = [&](const uint8_t* stage) {
+      return [=](int u) { return *reinterpret_cast<const uint4*>(stage + k_off + 16 * ((kcol0 + u) ^ (c & swz))); };
+    };
+    auto compute = [&](int st, const uint8_t* stage) {
+      if constexpr (KVF == FMT_E4M3_FNUZ) {
+        // The step's codes are read first; unless one of them is +-240 (rare:
+        // the extremes of the tensor), the OCP converter widens them, else
+        // the exact bit form does -- the two give identical values.
+        constexpr int KU = Cfg::DL * Cfg::KVB / 16;
+        uint4 kx[KU];
+        uint2 vx[Cfg::NDB / 2];
+        uint32_t hit = 0;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          kx[u] = k_lds(stage)(u);
+          hit |= e4m3fnuz_maxcode(kx[u].x) | e4m3fnuz_maxcode(kx[u].y) | e4m3fnuz_maxcode(kx[u].z) |
+                 e4m3fnuz_maxcode(kx[u].w);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::NDB / 2; ++i) {
+          vx[i] = lds_tr8(stage + v_off[i]);
+          hit |= e4m3fnuz_maxcode(vx[i].x) | e4m3fnuz_maxcode(vx[i].y);
+        }
+        auto kreg = [&](int u) { return kx[u]; };
+        auto vreg = [&](int i) { return vx[i]; };
+        if (__builtin_amdgcn_ballot_w64(hit != 0) == 0)
+          compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e4m3fnuz_ocp<MB>(w); });
+        else
+          compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4<MB, KVF>(w); });
+      } else {
+        compute_with(st, stage, k_lds(stage), [&](int i) { return lds_tr8(stage + v_off[i]); },
+                     [](uint32_t w) { return widen4<MB, KVF>(w); });
       }
     };
 

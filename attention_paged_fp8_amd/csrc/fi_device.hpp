@@ -87,6 +87,30 @@ __device__ __forceinline__ uint2 fnuz4(uint32_t w) {
   return r;
 }
 
+// Fast form for e4m3fnuz: apart from 0x7F / 0xFF (+-240, which OCP e4m3
+// reads as NaN) the same bits read as OCP e4m3 are exactly twice the fnuz
+// value (bias 7 against 8; 0x80 reads as -0 either way), so the OCP converter
+// with scale 2^-8 gives value * 2^-7 -- bit for bit what fnuz4 builds.  The
+// caller checks its codes with e4m3fnuz_maxcode first.
+template <bool QBF16>
+__device__ __forceinline__ uint2 widen4_e4m3fnuz_ocp(uint32_t w) {
+  constexpr float k = 0.00390625f;  // 2^-8
+  uint2 r;
+  if constexpr (QBF16) {
+    r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, k, false));
+    r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, k, true));
+  } else {
+    r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, k, false));
+    r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, k, true));
+  }
+  return r;
+}
+// Bit 7 of byte i of the result is set iff byte i of w is 0x7F or 0xFF (its
+// low 7 bits all ones: adding 1 carries into bit 7, and no byte carries out).
+__device__ __forceinline__ uint32_t e4m3fnuz_maxcode(uint32_t w) {
+  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+}
+
 // The two word_sel immediates must be compile-time constants.
 template <bool QBF16, int KVF>
 __device__ __forceinline__ uint2 widen4(uint32_t w) {

@@ -298,6 +298,50 @@ def test_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("plant", ["none", "some_steps"])
+@pytest.mark.parametrize("q", ["f16", "bf16"])
+def test_e4m3fnuz_extreme_codes(gpu_device, q, plant):
+    """e4m3fnuz decode widens through the OCP converter unless a wave's step
+    holds a +-240 code (0x7F / 0xFF), which OCP e4m3 reads as NaN; such steps
+    take the exact bit form.  With every extreme code removed (fast form
+    only) and with extremes planted in some steps of some requests (both
+    forms in one call), the output matches the oracle and is bit-identical to
+    the same values stored pre-widened in q's type."""
+    say("e4m3fnuz extremes", q, plant)
+    w = _mid_workload(kvd="e4m3fnuz", q=q)
+    kp, vp = w["k_pool"].copy(), w["v_pool"].copy()
+    pages_of = lambda i: w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
+    valid = np.zeros(kp.shape[:2], dtype=bool)  # (page, slot) holding a token of some request
+    for i, n in enumerate(w["kv_lens"]):
+        for t in range(int(n)):
+            valid[pages_of(i)[t // 16], t % 16] = True
+    for pool in (kp, vp):  # drop the extremes already present: +-240 -> +-224
+        sel = valid[:, :, None, None] & ((pool == 0x7F) | (pool == 0xFF))
+        pool[sel] = pool[sel] - 1
+    if plant == "some_steps":
+        rng = np.random.default_rng(5)
+        for i, n in enumerate(w["kv_lens"]):
+            for t in range(0, int(n), 48):  # one token in every third 16-token step
+                pg, sl = pages_of(i)[t // 16], t % 16
+                h, dd = rng.integers(0, 8), rng.integers(0, 128)
+                (kp if (t // 48) % 2 == 0 else vp)[pg, sl, h, dd] = 0x7F if rng.integers(0, 2) else 0xFF
+    w = dict(w, k_pool=kp, v_pool=vp)
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_decode(w, d)
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(o1, l1, o_ref, l_ref, q, f"e4m3fnuz extremes {plant}")
+    tab = fp8_table("e4m3fnuz")
+    kw = tab[kp].astype(np.float32)
+    vw = tab[vp].astype(np.float32)
+    kw[~np.isfinite(kw)] = np.nan
+    vw[~np.isfinite(vw)] = np.nan
+    k2 = torch.from_numpy(kw).to(T2[q]).to(gpu_device)
+    v2 = torch.from_numpy(vw).to(T2[q]).to(gpu_device)
+    kv, keep = paged_kv(w, d, k=k2, v=v2, kv_dtype=q)
+    o2, l2, _ = run_decode(w, d, kv=kv)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_kscale_fold(gpu_device):
     """Scaling k_scale by c equals scaling sm_scale by c; dropping the fold
     would fail the oracle comparison (the A/B check recorded in "fp8 KV cache in
