@@ -79,12 +79,9 @@ fi_status check_dtypes(const char* fn, fi_dtype q, fi_dtype* o, fi_dtype k, fi_d
   if (k == FI_I8 || k == FI_U8)
     return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be float16, "
                 "bfloat16, float8_e4m3fn or float8_e5m2", dtype_name(k));
-  if (prefill && (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ))
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; fnuz caches are read by the "
-                "decode calls only (prefill takes float8_e4m3fn / float8_e5m2)", dtype_name(k));
   if (!is_2byte(k) && !is_any_fp8(k))
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s; KV must be float16, bfloat16, float8_e4m3fn or float8_e5m2 "
-                "(decode also float8_e4m3fnuz / float8_e5m2fnuz)", dtype_name(k));
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s; KV must be float16, bfloat16, float8_e4m3fn, float8_e5m2, "
+                "float8_e4m3fnuz or float8_e5m2fnuz", dtype_name(k));
   if (prefill && is_2byte(k) && k != q)
     return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; prefill needs a 2-byte KV cache of the "
                 "query's dtype (fp8 KV is widened on load)", dtype_name(q), dtype_name(k));
@@ -110,8 +107,9 @@ fi_status check_dtypes_fp8q(const char* fn, fi_dtype q, fi_dtype o, fi_dtype k, 
     return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, which has no float interpretation; KV must be "
                 "float8_e4m3fn or float8_e5m2", dtype_name(k));
   if (!fnuz && (k == FI_F8_E4M3_FNUZ || k == FI_F8_E5M2_FNUZ))
-    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; fnuz caches are read by the "
-                "decode calls only", dtype_name(k));
+    return fail(FI_E_DTYPE, fn, "KV cache has dtype %s, the gfx942 fnuz variant; an fp8-query prefill runs the "
+                "OCP fp8 matrix cores on the raw codes (fnuz caches are read with a float16 or bfloat16 query, "
+                "or by fi_batch_decode_paged_fp8q)", dtype_name(k));
   if (!is_any_fp8(k))
     return fail(FI_E_DTYPE, fn, "q has dtype %s but the KV cache has dtype %s; an fp8 query needs an fp8 KV cache "
                 "(float8_e4m3fn or float8_e5m2)", dtype_name(q), dtype_name(k));
@@ -418,6 +416,11 @@ fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi
   p.n_qblocks = (int32_t)ceil_div(max_qo, p.q_per_wg);
   p.causal = causal ? 1 : 0;
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
+  // e4m3fnuz codes are widened to value * 2^-7 (exactly); the 2^7 joins the scales
+  if (kv_dtype == FI_F8_E4M3_FNUZ) {
+    k_scale *= 128.f;
+    v_scale *= 128.f;
+  }
   p.scale_log2 = scale * k_scale * fi::kLog2eHost;
   p.v_scale = v_scale;
   if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",

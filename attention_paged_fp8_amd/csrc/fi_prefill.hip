@@ -2,9 +2,10 @@
 //
 // What is computed: for every query token of every request and every q head,
 // softmax(q K^T * sm_scale) V over the keys the (optional) causal mask leaves
-// visible, with K and V stored as OCP fp8 or as q's 2-byte type
-// ("fp8 KV cache in the in-tree prefill kernel", AMD-Ecosystem/flashinfer
-// PR #368: Summary, Kernel, Benchmark results).  The causal mask is aligned to
+// visible, with K and V stored as OCP fp8, as the gfx942 fnuz fp8 layouts
+// (widened exactly from their bits) or as q's 2-byte type ("fp8 KV cache in
+// the in-tree prefill kernel", AMD-Ecosystem/flashinfer PR #368: Summary,
+// Kernel, Architecture / design notes, Benchmark results).  The causal mask is aligned to
 // the end of the KV sequence: row r sees key t iff t <= r + kv_len - qo_len.
 //
 // Mapping.  A workgroup of 8 waves owns one (request, kv head, group of heads,
@@ -66,8 +67,8 @@ namespace fi {
 // fp8 MFMA; the output is then normalised by the fp32 sum.
 template <bool QBF16, int KVF, bool OBF16, int D, bool Q8, bool P8 = false>
 struct PrefillCfg {
-  static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2);
-  static_assert(!Q8 || kFp8, "an fp8 query needs an fp8 KV cache");
+  static constexpr bool kFp8 = (KVF == FMT_E4M3 || KVF == FMT_E5M2 || KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ);
+  static_assert(!Q8 || KVF == FMT_E4M3 || KVF == FMT_E5M2, "an fp8 query needs an OCP fp8 KV cache");
   static_assert(!P8 || Q8, "fp8 P V needs the fp8 query path");
   static constexpr bool kP8 = P8;
   // The output is normalised by the sum of the probabilities as rounded for
@@ -661,12 +662,16 @@ hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_f
     switch (kv_fmt) {
       case FMT_BF16: return launch_prefill_o<FMT_BF16, FMT_BF16>(p, o_fmt, head_dim, batch, ragged, s);
       case FMT_E4M3: return launch_prefill_o<FMT_BF16, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+      case FMT_E4M3_FNUZ: return launch_prefill_o<FMT_BF16, FMT_E4M3_FNUZ>(p, o_fmt, head_dim, batch, ragged, s);
+      case FMT_E5M2_FNUZ: return launch_prefill_o<FMT_BF16, FMT_E5M2_FNUZ>(p, o_fmt, head_dim, batch, ragged, s);
       default: return launch_prefill_o<FMT_BF16, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
     }
   }
   switch (kv_fmt) {
     case FMT_F16: return launch_prefill_o<FMT_F16, FMT_F16>(p, o_fmt, head_dim, batch, ragged, s);
     case FMT_E4M3: return launch_prefill_o<FMT_F16, FMT_E4M3>(p, o_fmt, head_dim, batch, ragged, s);
+    case FMT_E4M3_FNUZ: return launch_prefill_o<FMT_F16, FMT_E4M3_FNUZ>(p, o_fmt, head_dim, batch, ragged, s);
+    case FMT_E5M2_FNUZ: return launch_prefill_o<FMT_F16, FMT_E5M2_FNUZ>(p, o_fmt, head_dim, batch, ragged, s);
     default: return launch_prefill_o<FMT_F16, FMT_E5M2>(p, o_fmt, head_dim, batch, ragged, s);
   }
 }

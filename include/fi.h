@@ -75,7 +75,8 @@
  * KV dtype, (prefill) 2-byte KV equal to q, then shapes, pointers, alignment,
  * page table and scales, then workspace.  The fp8-query calls check in the
  * same order with their own rules: q in {E4M3, E5M2}, o_dtype given
- * explicitly as F16 or BF16, k == v, an fp8 cache (fnuz in decode only),
+ * explicitly as F16 or BF16, k == v, an fp8 cache (fnuz in decode only: the
+ * fp8-query prefill feeds the raw codes to the OCP fp8 matrix cores),
  * then q_scale with the other scales.
  */
 #ifndef FI_H_
@@ -97,8 +98,8 @@ typedef enum fi_dtype {
   FI_F32 = 5,          /* refused everywhere */
   FI_I8 = 6,           /* refused: no float interpretation ([C] design notes) */
   FI_U8 = 7,           /* refused, as int8 */
-  FI_F8_E4M3_FNUZ = 8, /* the gfx942 variant, bias 8 ([C] design notes): decode only */
-  FI_F8_E5M2_FNUZ = 9  /* the gfx942 variant, bias 16: decode only */
+  FI_F8_E4M3_FNUZ = 8, /* the gfx942 variant, bias 8 ([C] design notes); not with an fp8-query prefill */
+  FI_F8_E5M2_FNUZ = 9  /* the gfx942 variant, bias 16; not with an fp8-query prefill */
 } fi_dtype;
 
 typedef enum fi_status {
@@ -144,7 +145,7 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
 /* Batched decode: one query token per request against its paged K/V.
  *   q        [dev] [batch, num_qo_heads, head_dim], q_dtype in {FI_F16, FI_BF16}
  *   kv       the paged cache; KV dtype in {F16, BF16, E4M3, E5M2, E4M3_FNUZ,
- *            E5M2_FNUZ} (fnuz: exact bit-level widening, decode only).  A 2-byte KV
+ *            E5M2_FNUZ} (fnuz: widened exactly, as in prefill).  A 2-byte KV
  *            dtype may differ from q's ([C] design notes: mixed 2-byte decode
  *            is correct); the products then run in bf16 with every fp16
  *            value split exactly into two bf16 parts, so nothing is rounded
@@ -184,7 +185,9 @@ fi_status fi_batch_decode_paged_fp8q(const void* q, fi_dtype q_dtype, float q_sc
  *   qo_indptr  [dev] [batch+1] query ranges; qo_indptr_h its [host] copy.
  *   causal     nonzero: mask aligned to the end of the KV sequence.
  *   A 2-byte KV dtype must equal q_dtype ([C] Refusals: prefill reads KV
- *   fragments as the query type); fp8 KV is widened on load.
+ *   fragments as the query type); fp8 KV -- OCP, or the gfx942 fnuz layouts
+ *   ([C] Architecture / design notes), widened exactly from their bits -- is
+ *   widened on load.
  *   workspace / workspace_bytes are unused (prefill does not split) and may be
  *   NULL / 0. */
 fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,

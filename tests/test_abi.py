@@ -152,8 +152,6 @@ DTYPE_REFUSALS = [
     ("decode", dict(k="i8"), 1, "KV cache has dtype int8, which has no float interpretation"),
     ("decode", dict(k="u8"), 1, "KV cache has dtype uint8, which has no float interpretation"),
     ("decode", dict(k="f32"), 1, "KV cache has dtype float32"),
-    ("prefill", dict(k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant; fnuz caches are read by the decode"),
-    ("prefill", dict(k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
     ("prefill", dict(q="f16", k="bf16"), 1,
      "fi_batch_prefill_paged: q has dtype float16 but the KV cache has dtype bfloat16; prefill needs a 2-byte KV"),
     ("prefill", dict(q="bf16", k="f16"), 1, "q has dtype bfloat16 but the KV cache has dtype float16"),
@@ -174,7 +172,7 @@ DTYPE_REFUSALS = [
     ("single_prefill", dict(q="bf16", k="f16"), 1,
      "fi_single_prefill: q has dtype bfloat16 but the KV cache has dtype float16"),
     ("single_prefill", dict(k="f16", v="bf16"), 1, "fi_single_prefill: k has dtype float16 but v has dtype bfloat16"),
-    ("single_prefill", dict(k="e5m2fnuz"), 1, "fi_single_prefill: KV cache has dtype float8_e5m2fnuz"),
+    ("single_prefill", dict(k="f32"), 1, "fi_single_prefill: KV cache has dtype float32"),
     ("single_prefill", dict(o="e4m3"), 1, "fi_single_prefill: o has dtype float8_e4m3fn"),
     ("fp8q", dict(q="f16", o="f16"), 1, "fi_batch_prefill_paged_fp8q: q has dtype float16; this call takes an fp8 query"),
     ("fp8q", dict(q="e4m3fnuz", o="f16"), 1, "q has dtype float8_e4m3fnuz; this call takes an fp8 query"),
@@ -184,7 +182,9 @@ DTYPE_REFUSALS = [
     ("fp8q", dict(q="e4m3", o="f16", k="f16"), 1,
      "q has dtype float8_e4m3fn but the KV cache has dtype float16; an fp8 query needs an fp8 KV cache"),
     ("fp8q", dict(q="e4m3", o="f16", k="u8"), 1, "KV cache has dtype uint8, which has no float interpretation"),
-    ("fp8q", dict(q="e4m3", o="f16", k="e5m2fnuz"), 1, "float8_e5m2fnuz, the gfx942 fnuz variant"),
+    ("fp8q", dict(q="e4m3", o="f16", k="e5m2fnuz"), 1,
+     "float8_e5m2fnuz, the gfx942 fnuz variant; an fp8-query prefill runs the OCP fp8 matrix cores"),
+    ("fp8q", dict(q="e5m2", o="bf16", k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant"),
 ]
 
 
@@ -231,6 +231,20 @@ def test_decode_accepts_fnuz_before_pointer_checks(L):
         kv, keep = _kv(k)
         assert _decode(L, kv) == 3 and "must not be NULL" in _err(L), _err(L)
         assert _single(L, k=k) == 3 and "must not be NULL" in _err(L), _err(L)
+
+
+@no_gpu
+def test_prefill_accepts_fnuz_before_pointer_checks(L):
+    """fnuz caches pass the dtype checks of the prefill calls that take a
+    2-byte query -- paged, ragged and single (the next refusal is the NULL
+    pointer) -- while the fp8-query prefill refuses them."""
+    for k in ("e4m3fnuz", "e5m2fnuz"):
+        for q in ("f16", "bf16"):
+            kv, keep = _kv(k)
+            assert _prefill(L, kv, q=q) == 3 and "must not be NULL" in _err(L), _err(L)
+            kr, keepr = _ragged(k, k)
+            assert _prefill_ragged(L, kr, q=q) == 3 and "must not be NULL" in _err(L), _err(L)
+            assert _single_prefill(L, q=q, k=k, v=k) == 3 and "must not be NULL" in _err(L), _err(L)
 
 
 @no_gpu

@@ -245,13 +245,17 @@ def test_decode_fp8_query(gpu_device, case):
     assert np.max(np.abs(og - o2)) <= O_TOL[o] and np.max(np.abs(lg[np.isfinite(lg)] - l2[np.isfinite(l2)])) <= 1e-3
 
 
-def test_prefill_refuses_fnuz(gpu_device):
-    w = make_paged(8, qo_lens=[4], prefix_lens=[10], hq=8, hkv=2, d=64, page=16, q="f16", kvd="e4m3fnuz")
+def test_fp8q_prefill_refuses_fnuz(gpu_device):
+    """The fp8-query prefill runs the OCP fp8 matrix cores on the raw cache
+    codes, so it refuses an fnuz cache with a sentence and leaves o as it was
+    (the 2-byte-query prefill reads fnuz caches: test_gpu_prefill)."""
+    w = make_paged(8, qo_lens=[4], prefix_lens=[10], hq=8, hkv=2, d=64, page=16, q="e4m3", kvd="e4m3fnuz", o="f16")
     d = upload(w, gpu_device)
     kv, keep = paged_kv(w, d)
     o = torch.full((4, 8, 64), 7.0, dtype=torch.float16, device=gpu_device)
-    with pytest.raises(fi.FiValueError, match="fnuz caches are read by the decode calls only"):
-        fi.fi_batch_prefill_paged(d["q"], d["qo_indptr"], kv, o, qo_indptr_h=w["qo_indptr"])
+    with pytest.raises(fi.FiValueError, match="an fp8-query prefill runs the OCP fp8 matrix cores"):
+        fi.fi_batch_prefill_paged_fp8q(d["q"], d["qo_indptr"], kv, o, q_dtype="e4m3", q_scale=w["q_scale"],
+                                       qo_indptr_h=w["qo_indptr"])
     torch.cuda.synchronize()
     assert torch.all(o == 7.0)
 

@@ -8,7 +8,8 @@ small shapes (GQA groups 1, 2, 3, 4, 8, 32; head_dim 64 and 128; page sizes 1 to
 prefix lengths that leave partial tiles); rows with no visible key; requests
 without queries or without keys; decode equal to prefill with one query per
 request; run-to-run determinism and page-permutation invariance (bitwise);
-fp8 equal to the same values stored in the 2-byte type (bitwise); constant V;
+fp8 (OCP and fnuz) equal to the same values stored in the 2-byte type
+(bitwise); fnuz caches in the shape matrix; constant V;
 a head-major pool through its strides.
 """
 import numpy as np
@@ -37,6 +38,11 @@ SMALL = [
     ("e4m3", "f16", "f16", 16, 128, 32, 1, (65, 3), (100, 0), True),       # group 32: 8 head subgroups
     ("e5m2", "bf16", "bf16", 1, 64, 2, 2, (300,), (0,), True),             # page 1, one q head per kv head
     ("e4m3", "f16", "f16", 16, 128, 8, 8, (700,), (1300,), False),         # long non-causal with a prefix
+    # fnuz caches (the gfx942 layouts; widened exactly from the bits)
+    ("e4m3fnuz", "f16", "f16", 16, 128, 32, 8, (1, 37, 130, 64), (0, 100, 5, 300), True),
+    ("e4m3fnuz", "bf16", "bf16", 4, 64, 8, 2, (129, 3), (1, 64), False),
+    ("e5m2fnuz", "bf16", "f16", 64, 128, 16, 8, (200, 33), (70, 0), True),
+    ("e5m2fnuz", "f16", "bf16", 1, 64, 12, 4, (45, 90), (10, 0), True),
 ]
 
 
@@ -123,7 +129,7 @@ def test_prefill_page_permutation_bitwise(gpu_device):
     assert_parity(o1, l1, o_ref, l_ref, "f16", "prefill page permutation")
 
 
-@pytest.mark.parametrize("kvd,q", [("e4m3", "f16"), ("e5m2", "bf16")])
+@pytest.mark.parametrize("kvd,q", [("e4m3", "f16"), ("e5m2", "bf16"), ("e4m3fnuz", "bf16"), ("e5m2fnuz", "f16")])
 def test_prefill_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
     """fp8 K/V give bit-identical output to the same values stored widened in
     q's 2-byte type (the tiles the kernel builds are the same)."""

@@ -37,6 +37,8 @@ CASES = [
     ("e5m2", "f16", "bf16", 64, 12, 4, (45, 90), (10, 0), True),
     ("f16", "f16", "f16", 128, 32, 8, (77, 256), (3, 128), True),
     ("bf16", "bf16", "bf16", 64, 4, 2, (150,), (200,), False),
+    ("e4m3fnuz", "bf16", "bf16", 128, 32, 8, (1, 37, 130), (0, 100, 5), True),
+    ("e5m2fnuz", "f16", "f16", 64, 8, 2, (129, 3), (1, 64), False),
 ]
 
 
@@ -112,6 +114,7 @@ SINGLE = [
     ("e4m3", "bf16", 64, 4, 4, 130, 130, False),
     ("f16", "f16", 64, 12, 4, 77, 40, True),    # kv shorter than qo: early rows see nothing
     ("e4m3", "f16", 128, 16, 8, 64, 0, True),   # no keys
+    ("e4m3fnuz", "f16", 128, 32, 8, 200, 700, True),
 ]
 
 
