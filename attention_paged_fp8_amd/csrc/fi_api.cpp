@@ -655,17 +655,23 @@ fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_s
                      reinterpret_cast<hipStream_t>(stream));
 }
 
-fi_status fi_batch_prefill_ragged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
-                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
-                                  const fi_ragged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
-                                  float sm_scale, void* stream) {
-  static const char* fn = "fi_batch_prefill_ragged";
+}  // extern "C"
+
+// Ragged and single prefill, with a 2-byte query or (q8) an fp8 query with
+// its q_scale, which joins k_scale in the logit scale as in the paged call.
+static fi_status ragged_prefill(const char* fn, bool q8, const void* q, fi_dtype q_dtype, float q_scale,
+                                const int32_t* qo_indptr, const int32_t* qo_indptr_h, int32_t batch,
+                                int32_t num_qo_heads, const fi_ragged_kv* kv, int32_t causal, int32_t pv_fp8, void* o,
+                                fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
   if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
-  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, true);
+  fi_status st = q8 ? check_dtypes_fp8q(fn, q_dtype, o_dtype, kv->k_dtype, kv->v_dtype)
+                    : check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, true);
   if (st != FI_OK) return st;
   if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is negative", batch);
   if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
   if (batch > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  if (q8 && (!std::isfinite(q_scale) || !(q_scale > 0.f)))
+    return fail(FI_E_ARG, fn, "q_scale=%g must be finite and > 0", q_scale);
   if ((st = check_scales(fn, kv->k_scale, kv->v_scale, sm_scale)) != FI_OK) return st;
   if (kv->num_tokens < 0) return fail(FI_E_SHAPE, fn, "num_tokens=%d is negative", kv->num_tokens);
   if ((st = check_rows(fn, kv->k, kv->v, kv->k_dtype, kv->stride_token, kv->stride_head,
@@ -698,21 +704,25 @@ fi_status fi_batch_prefill_ragged(const void* q, fi_dtype q_dtype, const int32_t
   p.sh = kv->stride_head * eb;
   p.qo_indptr = qo_indptr;
   p.indptr = kv->indptr;
+  p.pv_fp8 = (q8 && pv_fp8) ? 1 : 0;
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
-                     causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale, kv->v_scale, true,
-                     reinterpret_cast<hipStream_t>(stream));
+                     causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * (q8 ? q_scale : 1.0f), kv->v_scale,
+                     true, reinterpret_cast<hipStream_t>(stream));
 }
 
-fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, const void* k, const void* v,
-                            fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t causal, float k_scale, float v_scale,
-                            void* o, fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
-  static const char* fn = "fi_single_prefill";
-  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, k_dtype, v_dtype, true);
+static fi_status single_prefill(const char* fn, bool q8, const void* q, fi_dtype q_dtype, float q_scale,
+                                int32_t qo_len, const void* k, const void* v, fi_dtype k_dtype, fi_dtype v_dtype,
+                                int32_t kv_len, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t causal, int32_t pv_fp8, float k_scale, float v_scale, void* o,
+                                fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
+  fi_status st = q8 ? check_dtypes_fp8q(fn, q_dtype, o_dtype, k_dtype, v_dtype)
+                    : check_dtypes(fn, q_dtype, &o_dtype, k_dtype, v_dtype, true);
   if (st != FI_OK) return st;
   if ((st = check_heads(fn, num_qo_heads, num_kv_heads, head_dim)) != FI_OK) return st;
   if (qo_len < 0) return fail(FI_E_SHAPE, fn, "qo_len=%d is negative", qo_len);
   if (kv_len < 0 || kv_len >= (1 << 30)) return fail(FI_E_SHAPE, fn, "kv_len=%d is outside [0, 2^30)", kv_len);
+  if (q8 && (!std::isfinite(q_scale) || !(q_scale > 0.f)))
+    return fail(FI_E_ARG, fn, "q_scale=%g must be finite and > 0", q_scale);
   if ((st = check_scales(fn, k_scale, v_scale, sm_scale)) != FI_OK) return st;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if ((st = check_rows(fn, k, v, k_dtype, row, head_dim, kv_len)) != FI_OK) return st;
@@ -732,12 +742,50 @@ fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, con
   p.sh = (int64_t)head_dim * eb;
   p.single_qo_len = qo_len;
   p.single_kv_len = kv_len;
+  p.pv_fp8 = (q8 && pv_fp8) ? 1 : 0;
   const int32_t qo_indptr_h[2] = {0, qo_len};
   const std::vector<int64_t> lens(1, kv_len);
   return run_prefill(fn, p, q_dtype, k_dtype, o_dtype, 1, num_qo_heads, num_kv_heads, head_dim, causal, qo_len,
-                     qo_indptr_h, lens, sm_scale, k_scale, v_scale, true, reinterpret_cast<hipStream_t>(stream));
+                     qo_indptr_h, lens, sm_scale, k_scale * (q8 ? q_scale : 1.0f), v_scale, true,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
+extern "C" {
+
+fi_status fi_batch_prefill_ragged(const void* q, fi_dtype q_dtype, const int32_t* qo_indptr,
+                                  const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                  const fi_ragged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
+                                  float sm_scale, void* stream) {
+  return ragged_prefill("fi_batch_prefill_ragged", false, q, q_dtype, 1.0f, qo_indptr, qo_indptr_h, batch,
+                        num_qo_heads, kv, causal, 0, o, o_dtype, lse, sm_scale, stream);
+}
+
+fi_status fi_batch_prefill_ragged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
+                                       const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                       const fi_ragged_kv* kv, int32_t causal, int32_t pv_fp8, void* o,
+                                       fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
+  return ragged_prefill("fi_batch_prefill_ragged_fp8q", true, q, q_dtype, q_scale, qo_indptr, qo_indptr_h, batch,
+                        num_qo_heads, kv, causal, pv_fp8, o, o_dtype, lse, sm_scale, stream);
+}
+
+fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, const void* k, const void* v,
+                            fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t causal, float k_scale, float v_scale,
+                            void* o, fi_dtype o_dtype, float* lse, float sm_scale, void* stream) {
+  return single_prefill("fi_single_prefill", false, q, q_dtype, 1.0f, qo_len, k, v, k_dtype, v_dtype, kv_len,
+                        num_qo_heads, num_kv_heads, head_dim, causal, 0, k_scale, v_scale, o, o_dtype, lse, sm_scale,
+                        stream);
+}
+
+fi_status fi_single_prefill_fp8q(const void* q, fi_dtype q_dtype, float q_scale, int32_t qo_len, const void* k,
+                                 const void* v, fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len,
+                                 int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
+                                 int32_t pv_fp8, float k_scale, float v_scale, void* o, fi_dtype o_dtype, float* lse,
+                                 float sm_scale, void* stream) {
+  return single_prefill("fi_single_prefill_fp8q", true, q, q_dtype, q_scale, qo_len, k, v, k_dtype, v_dtype, kv_len,
+                        num_qo_heads, num_kv_heads, head_dim, causal, pv_fp8, k_scale, v_scale, o, o_dtype, lse,
+                        sm_scale, stream);
+}
 
 fi_status fi_fp8_widen(const uint8_t* codes, int64_t n, fi_dtype src, fi_dtype dst, void* out, void* stream) {
   static const char* fn = "fi_fp8_widen";

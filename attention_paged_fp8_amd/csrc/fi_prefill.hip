@@ -616,12 +616,18 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int batch, bool ragge
   const int nsg = p.group / p.heads_per_wg;
   const dim3 grid = (p.n_items > 0) ? dim3(p.n_items * p.num_kv_heads * nsg, 1)
                                     : dim3(batch * p.num_kv_heads * nsg, p.n_qblocks);
-  if constexpr (QF == FMT_E4M3 || QF == FMT_E5M2) {  // fp8 queries: paged calls only
-    if (ragged) return hipErrorInvalidValue;
-    if (p.pv_fp8)
-      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
-    else
-      hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+  if constexpr (QF == FMT_E4M3 || QF == FMT_E5M2) {
+    if (p.pv_fp8) {
+      if (ragged)
+        hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, true, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, true>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+    } else {
+      if (ragged)
+        hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, true, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<QF, KVF, OBF16, D, false, false>), grid, dim3(64 * kPrefillWaves), 0, s, p);
+    }
   } else {
     if (p.pv_fp8) return hipErrorInvalidValue;
     if (ragged)

@@ -35,8 +35,9 @@ STATUS = {0: "FI_OK", 1: "FI_E_DTYPE", 2: "FI_E_SHAPE", 3: "FI_E_ARG", 4: "FI_E_
 
 # every symbol include/fi.h declares
 EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_decode_paged_fp8q",
-           "fi_batch_prefill_paged",
-           "fi_batch_prefill_paged_fp8q", "fi_batch_prefill_ragged", "fi_single_prefill", "fi_single_decode", "fi_fp8_widen")
+           "fi_batch_prefill_paged", "fi_batch_prefill_paged_fp8q", "fi_batch_prefill_ragged",
+           "fi_batch_prefill_ragged_fp8q", "fi_single_prefill", "fi_single_prefill_fp8q", "fi_single_decode",
+           "fi_fp8_widen")
 
 
 class FiError(Exception):
@@ -110,6 +111,12 @@ def lib() -> ctypes.CDLL:
     L.fi_batch_prefill_ragged.restype = en
     L.fi_batch_prefill_ragged.argtypes = [vp, en, vp, vp, i32, i32, ctypes.POINTER(RaggedKV), i32, vp, en, vp, f32,
                                           vp]
+    L.fi_batch_prefill_ragged_fp8q.restype = en
+    L.fi_batch_prefill_ragged_fp8q.argtypes = [vp, en, f32, vp, vp, i32, i32, ctypes.POINTER(RaggedKV), i32, i32, vp,
+                                               en, vp, f32, vp]
+    L.fi_single_prefill_fp8q.restype = en
+    L.fi_single_prefill_fp8q.argtypes = [vp, en, f32, i32, vp, vp, en, en, i32, i32, i32, i32, i32, i32, f32, f32, vp,
+                                         en, vp, f32, vp]
     L.fi_single_prefill.restype = en
     L.fi_single_prefill.argtypes = [vp, en, i32, vp, vp, en, en, i32, i32, i32, i32, i32, f32, f32, vp, en, vp, f32,
                                     vp]
@@ -279,6 +286,37 @@ def fi_batch_prefill_ragged(q, qo_indptr, kv: RaggedKV, o, *, causal=True, q_dty
         int(batch if batch is not None else qh.numel() - 1), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
         ctypes.byref(kv), 1 if causal else 0, _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse),
         float(sm_scale), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def fi_batch_prefill_ragged_fp8q(q, qo_indptr, kv: RaggedKV, o, *, q_dtype, o_dtype=None, q_scale=1.0, causal=True,
+                                 pv_fp8=False, lse=None, sm_scale=0.0, qo_indptr_h=None, batch=None, num_qo_heads=None,
+                                 stream=None):
+    """q [total_q, H_qo, D] fp8 codes (a float8 tensor, or uint8 with q_dtype
+    naming the format); o [total_q, H_qo, D] float16 or bfloat16."""
+    qh = _host_i32(qo_indptr_h if qo_indptr_h is not None else qo_indptr)
+    st = lib().fi_batch_prefill_ragged_fp8q(
+        _ptr(q), _dt(q_dtype), float(q_scale), _ptr(qo_indptr), qh.data_ptr(),
+        int(batch if batch is not None else qh.numel() - 1), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
+        ctypes.byref(kv), 1 if causal else 0, 1 if pv_fp8 else 0, _ptr(o),
+        _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def fi_single_prefill_fp8q(q, k, v, o, *, q_dtype, q_scale=1.0, causal=True, pv_fp8=False, k_scale=1.0, v_scale=1.0,
+                           kv_dtype=None, k_dtype=None, v_dtype=None, o_dtype=None, lse=None, sm_scale=0.0,
+                           stream=None):
+    """q [qo_len, H_qo, D] fp8 codes; k and v contiguous [kv_len, H_kv, D] fp8
+    codes; o [qo_len, H_qo, D] float16 or bfloat16."""
+    kd = k_dtype if k_dtype is not None else (kv_dtype if kv_dtype is not None else k.dtype)
+    vd = v_dtype if v_dtype is not None else (kv_dtype if kv_dtype is not None else v.dtype)
+    st = lib().fi_single_prefill_fp8q(
+        _ptr(q), _dt(q_dtype), float(q_scale), int(q.shape[0]), _ptr(k), _ptr(v), _dt(kd), _dt(vd), int(k.shape[0]),
+        int(q.shape[1]), int(k.shape[1]), int(k.shape[2]), 1 if causal else 0, 1 if pv_fp8 else 0, float(k_scale),
+        float(v_scale), _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale),
+        _stream(stream, q, o))
     check(st)
     return o
 

@@ -3,8 +3,9 @@
  * paged KV cache, decode and causal prefill, with fp16/bf16 queries and
  * outputs and K/V stored as OCP fp8 (e4m3 or e5m2) with per-tensor scales,
  * widened to the query's 2-byte type as they are loaded.  Beside these: fp8
- * queries with a per-tensor q_scale (the *_fp8q calls), fnuz fp8 caches in
- * decode, and prefill over ragged (non-paged) K/V or a single request.
+ * queries with a per-tensor q_scale (the *_fp8q calls), fnuz fp8 caches
+ * (decode, and prefill with a 2-byte query), and prefill over ragged
+ * (non-paged) K/V or a single request.
  *
  * The problem statement these calls follow comes from three pages:
  *   [A] "Enable Hopper FA3 FP8 attention in decode.py" (flashinfer PR #2148):
@@ -265,6 +266,22 @@ fi_status fi_single_prefill(const void* q, fi_dtype q_dtype, int32_t qo_len, con
                             fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len, int32_t num_qo_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t causal, float k_scale, float v_scale,
                             void* o, fi_dtype o_dtype, float* lse, float sm_scale, void* stream);
+
+/* The ragged and single prefill calls with an fp8 query: q holds e4m3 / e5m2
+ * codes with a per-tensor q_scale (real q = code * q_scale), o_dtype is given
+ * explicitly as F16 or BF16, and the cache is OCP fp8 -- the dtype rules,
+ * q_scale fold and pv_fp8 mode of fi_batch_prefill_paged_fp8q, with the K/V
+ * addressing of fi_batch_prefill_ragged / fi_single_prefill.  Over the same
+ * values a ragged, single and paged fp8-query call give identical bits. */
+fi_status fi_batch_prefill_ragged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
+                                       const int32_t* qo_indptr_h, int32_t batch, int32_t num_qo_heads,
+                                       const fi_ragged_kv* kv, int32_t causal, int32_t pv_fp8, void* o,
+                                       fi_dtype o_dtype, float* lse, float sm_scale, void* stream);
+fi_status fi_single_prefill_fp8q(const void* q, fi_dtype q_dtype, float q_scale, int32_t qo_len, const void* k,
+                                 const void* v, fi_dtype k_dtype, fi_dtype v_dtype, int32_t kv_len,
+                                 int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
+                                 int32_t pv_fp8, float k_scale, float v_scale, void* o, fi_dtype o_dtype, float* lse,
+                                 float sm_scale, void* stream);
 
 /* Decode of one query against a contiguous K/V ([C] Summary: the single-decode
  * entry point).  k and v are [dev] [kv_len, num_kv_heads, head_dim] with the

@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -135,6 +135,18 @@ def _prefill_fp8q(L, kv, q="e4m3", o="f16", hq=4, batch=2, qp=None, op=None, q_s
                                          1, 0, op, fi.DTYPES[o], None, 0.0, None)
 
 
+def _ragged_fp8q(L, kv, q="e4m3", o="f16", hq=4, batch=2, qp=None, op=None, q_scale=1.0, qo_dev=None):
+    qo = np.array([0, 3, 7], np.int32)
+    return L.fi_batch_prefill_ragged_fp8q(qp, fi.DTYPES[q], q_scale, qo_dev, qo.ctypes.data, batch, hq,
+                                          ctypes.byref(kv), 1, 1, op, fi.DTYPES[o], None, 0.0, None)
+
+
+def _single_fp8q(L, q="e4m3", k="e4m3", v=None, o="f16", d=64, hq=4, hkv=2, qo_len=5, kv_len=8, qp=None, kp=None,
+                 op=None, q_scale=1.0):
+    return L.fi_single_prefill_fp8q(qp, fi.DTYPES[q], q_scale, qo_len, kp, kp, fi.DTYPES[k], fi.DTYPES[v or k], kv_len,
+                                    hq, hkv, d, 1, 0, 1.0, 1.0, op, fi.DTYPES[o], None, 0.0, None)
+
+
 def _err(L):
     return L.fi_last_error().decode()
 
@@ -185,6 +197,16 @@ DTYPE_REFUSALS = [
     ("fp8q", dict(q="e4m3", o="f16", k="e5m2fnuz"), 1,
      "float8_e5m2fnuz, the gfx942 fnuz variant; an fp8-query prefill runs the OCP fp8 matrix cores"),
     ("fp8q", dict(q="e5m2", o="bf16", k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant"),
+    ("ragged_fp8q", dict(q="f16", o="f16"), 1, "fi_batch_prefill_ragged_fp8q: q has dtype float16; this call takes an"),
+    ("ragged_fp8q", dict(q="e4m3", o="default"), 1, "fi_batch_prefill_ragged_fp8q: o_dtype must be given"),
+    ("ragged_fp8q", dict(q="e4m3", o="f16", k="e4m3fnuz"), 1, "float8_e4m3fnuz, the gfx942 fnuz variant"),
+    ("ragged_fp8q", dict(q="e4m3", o="f16", k="bf16"), 1, "an fp8 query needs an fp8 KV cache"),
+    ("ragged_fp8q", dict(q="e5m2", o="e4m3"), 1, "an fp8 output is not supported"),
+    ("single_fp8q", dict(q="bf16", o="bf16"), 1, "fi_single_prefill_fp8q: q has dtype bfloat16; this call takes an"),
+    ("single_fp8q", dict(q="e4m3", o="f16", k="e4m3", v="e5m2"), 1, "k has dtype float8_e4m3fn but v has dtype"),
+    ("single_fp8q", dict(q="e4m3", o="f16", k="e5m2fnuz"), 1, "fi_single_prefill_fp8q: KV cache has dtype "
+     "float8_e5m2fnuz, the gfx942 fnuz variant"),
+    ("single_fp8q", dict(q="e4m3", o="f16", k="i8"), 1, "no float interpretation"),
 ]
 
 
@@ -202,6 +224,11 @@ def test_dtype_refusals(L, call, kw, status, frag):
     elif call == "fp8q":
         kv, keep = _kv(k, v)
         st = _prefill_fp8q(L, kv, q=q, o=o)
+    elif call == "ragged_fp8q":
+        kv, keep = _ragged(k, v)
+        st = _ragged_fp8q(L, kv, q=q, o=o)
+    elif call == "single_fp8q":
+        st = _single_fp8q(L, q=q, k=k, v=v, o=o)
     elif call == "ragged":
         kv, keep = _ragged(k, v)
         st = _prefill_ragged(L, kv, q=q, o=o)
@@ -245,6 +272,18 @@ def test_prefill_accepts_fnuz_before_pointer_checks(L):
             kr, keepr = _ragged(k, k)
             assert _prefill_ragged(L, kr, q=q) == 3 and "must not be NULL" in _err(L), _err(L)
             assert _single_prefill(L, q=q, k=k, v=k) == 3 and "must not be NULL" in _err(L), _err(L)
+
+
+@no_gpu
+def test_ragged_and_single_fp8q_reach_pointer_checks(L):
+    """Valid fp8-query ragged and single calls pass every dtype, shape and
+    scale check and stop at the NULL pointers; a bad q_scale is refused first."""
+    kv, keep = _ragged("e5m2")
+    assert _ragged_fp8q(L, kv) == 3 and "must not be NULL" in _err(L), _err(L)
+    assert _ragged_fp8q(L, kv, q_scale=0.0, qo_dev=0x10000) == 3 and "q_scale=0 must be finite and > 0" in _err(L), \
+        _err(L)
+    assert _single_fp8q(L, k="e5m2") == 3 and "must not be NULL" in _err(L), _err(L)
+    assert _single_fp8q(L, q_scale=float("nan")) == 3 and "q_scale=nan" in _err(L), _err(L)
 
 
 @no_gpu

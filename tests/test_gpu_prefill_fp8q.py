@@ -225,3 +225,43 @@ def test_config3_fp8q_pv8_sampled_rows(gpu_device):
     err = np.abs(og[a:b] - o_ref)
     assert np.all(err <= bound), f"request {i}: max excess {float(np.max(err - bound)):.3e}"
     assert float(np.max(np.abs(lg[a:b] - l_ref))) <= LSE_TOL
+
+
+@pytest.mark.parametrize("pv8", [False, True])
+@pytest.mark.parametrize("q,kvd", [("e4m3", "e4m3"), ("e5m2", "e5m2")])
+def test_ragged_and_single_fp8q_equal_paged(gpu_device, q, kvd, pv8):
+    """fi_batch_prefill_ragged_fp8q over the same K/V values stored
+    contiguously per request, and fi_single_prefill_fp8q on one request, give
+    the bits of fi_batch_prefill_paged_fp8q (the same kernel, addressing rows
+    instead of pages); the 16-bit P V mode also against the oracle."""
+    say("ragged/single fp8q", q, kvd, pv8)
+    from workloads import ragged_rows
+    w = make_paged(61, qo_lens=[1, 70, 300, 129], prefix_lens=[0, 45, 600, 3], hq=32, hkv=8, d=128, page=16, q=q,
+                   kvd=kvd, o="f16")
+    d = upload(w, gpu_device)
+    op, lp = run_fp8q(w, d, causal=True, pv_fp8=pv8)
+    if not pv8:
+        o_ref, l_ref = OA.batch_prefill(w, causal=True)
+        assert_parity(op, lp, o_ref, l_ref, "f16", "paged fp8q")
+    kr, vr, indptr = ragged_rows(w, lead=3, tail=2)
+    kt, vt = torch.from_numpy(kr).to(gpu_device), torch.from_numpy(vr).to(gpu_device)
+    ind = torch.from_numpy(indptr).to(gpu_device)
+    kv, keep = fi.make_ragged_kv(kt, vt, ind, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=kvd, indptr_h=indptr)
+    T, H, D = int(w["qo_indptr"][-1]), w["num_qo_heads"], w["head_dim"]
+    o = torch.full((T, H, D), float("nan"), dtype=torch.float16, device=gpu_device)
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device=gpu_device)
+    fi.fi_batch_prefill_ragged_fp8q(d["q"], d["qo_indptr"], kv, o, q_dtype=q, q_scale=w["q_scale"], causal=True,
+                                    pv_fp8=pv8, lse=lse, qo_indptr_h=w["qo_indptr"])
+    torch.cuda.synchronize()
+    assert np.array_equal(o.double().cpu().numpy(), op) and np.array_equal(lse.double().cpu().numpy(), lp)
+    # one request (the third) through the single call
+    i = 2
+    q0, q1 = int(w["qo_indptr"][i]), int(w["qo_indptr"][i + 1])
+    a, e = int(indptr[i]), int(indptr[i + 1])
+    ks, vs = kt[a:e].contiguous(), vt[a:e].contiguous()
+    o1 = torch.full((q1 - q0, H, D), float("nan"), dtype=torch.float16, device=gpu_device)
+    l1 = torch.full((q1 - q0, H), float("nan"), dtype=torch.float32, device=gpu_device)
+    fi.fi_single_prefill_fp8q(d["q"][q0:q1].contiguous(), ks, vs, o1, q_dtype=q, q_scale=w["q_scale"], causal=True,
+                              pv_fp8=pv8, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=kvd, lse=l1)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1.double().cpu().numpy(), op[q0:q1]) and np.array_equal(l1.double().cpu().numpy(), lp[q0:q1])
