@@ -10,7 +10,9 @@ bitwise determinism, bitwise page-permutation invariance, an fp8 run equal
 bitwise to a run on the same values pre-widened to q's type (the equivalence
 design of "fp8 KV cache in the in-tree prefill kernel", Test plan), the
 k_scale fold, constant V, NaN-poisoned padding and unreferenced pages, and a
-non-default (head-major) pool layout.
+non-default (head-major) pool layout; batches past the planner's limits (900
+requests: prefix sums scanned on the device; 1100: fixed chunks) and a
+page-size-1 request spanning three page-id windows.
 """
 import numpy as np
 import pytest
@@ -416,3 +418,33 @@ def test_split_and_unsplit_agree(gpu_device):
         assert_parity(o, l, o_ref, l_ref, "bf16", f"split={split}")
     o, l, _ = run_decode(w, d, workspace=False)
     assert_parity(o, l, o_ref, l_ref, "bf16", "no workspace")
+
+
+@pytest.mark.parametrize("batch", [900, 1100])
+def test_decode_large_batch(gpu_device, batch):
+    """Batches past the limits of the planner's fast paths: above 768
+    requests the token prefix sums no longer travel in the kernel arguments
+    and every workgroup scans the page table itself; above 1024 the planner
+    falls back to fixed chunks.  Short, ragged requests (some empty) against
+    the oracle."""
+    say("decode large batch", batch)
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(0, 300, size=batch)
+    lens[::97] = 0
+    w = make_paged(batch, kv_lens=list(lens), hq=8, hkv=2, d=64, page=16, q="bf16", kvd="e4m3")
+    d = upload(w, gpu_device)
+    og, lg, _ = run_decode(w, d)
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(og, lg, o_ref, l_ref, "bf16", f"decode batch {batch}")
+
+
+def test_decode_page1_many_windows(gpu_device):
+    """page_size 1 with 2500 pages in one request: the page ids are staged in
+    three LDS windows of 1024 pages."""
+    say("decode page 1, 2500 pages")
+    w = make_paged(41, kv_lens=[2500, 7, 1100], hq=16, hkv=4, d=128, page=1, q="f16", kvd="e5m2")
+    d = upload(w, gpu_device)
+    for split in (None, "128"):
+        og, lg, _ = run_decode(w, d, split=split)
+        o_ref, l_ref = OA.batch_decode(w)
+        assert_parity(og, lg, o_ref, l_ref, "f16", f"decode page 1, split {split}")

@@ -10,7 +10,8 @@ without queries or without keys; decode equal to prefill with one query per
 request; run-to-run determinism and page-permutation invariance (bitwise);
 fp8 (OCP and fnuz) equal to the same values stored in the 2-byte type
 (bitwise); fnuz caches in the shape matrix; constant V;
-a head-major pool through its strides.
+a head-major pool through its strides; 800 requests, more (request, query
+block) pairs than the dispatch order in the kernel arguments holds.
 """
 import numpy as np
 import pytest
@@ -188,3 +189,18 @@ def test_prefill_requests_without_queries_or_keys(gpu_device, causal):
     assert np.all(o[0:40] == 0) and np.all(np.isneginf(l[0:40]))
     o_ref, l_ref = OA.batch_prefill(w, causal=causal)
     assert_parity(o, l, o_ref, l_ref, "bf16", "prefill empty requests")
+
+
+def test_prefill_many_query_blocks(gpu_device):
+    """More (request, query block) pairs than the dispatch order carried in the
+    kernel arguments holds (768): the kernel then walks the grid in request
+    order.  800 short requests, one query block each, against the oracle."""
+    say("prefill 800 requests")
+    rng = np.random.default_rng(800)
+    qo = rng.integers(1, 65, size=800)
+    prefix = rng.integers(0, 100, size=800)
+    w = make_paged(800, qo_lens=list(qo), prefix_lens=list(prefix), hq=8, hkv=8, d=64, page=16, q="f16", kvd="e4m3")
+    d = upload(w, gpu_device)
+    og, lg, _ = run_prefill(w, d, causal=True)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert_parity(og, lg, o_ref, l_ref, "f16", "prefill 800 requests")
