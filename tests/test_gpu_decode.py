@@ -87,11 +87,13 @@ SMALL = [
     ("bf16", "f16", "f16", 16, 128, 32, 8, (600, 90), "128"),        # mixed 2-byte decode
     ("f16", "bf16", "bf16", 8, 128, 8, 8, (300, 12), None),          # mixed the other way
     ("e5m2", "f16", "f16", 2, 128, 16, 16, (55, 1, 0, 1024), "128"),
-    # fnuz caches (decode only)
+    # fnuz caches
     ("e4m3fnuz", "f16", "f16", 16, 128, 32, 8, (1, 31, 32, 33, 200, 517, 0, 64), None),
     ("e4m3fnuz", "bf16", "bf16", 16, 128, 32, 8, (700, 129, 5), "128"),
     ("e5m2fnuz", "f16", "bf16", 64, 128, 64, 8, (1000, 3, 2049), "256"),
     ("e5m2fnuz", "bf16", "f16", 4, 64, 8, 2, (77, 300, 1), None),
+    ("e4m3fnuz", "bf16", "f16", 4, 64, 8, 2, (77, 300, 1), None),
+    ("e4m3fnuz", "f16", "bf16", 32, 64, 16, 16, (55, 1, 0, 1024), "128"),
 ]
 
 
