@@ -156,14 +156,14 @@ def _graph_calls(fn, n_copies, steps, warmup):
     return wall_ms
 
 
-def run_decode_bench(steps, warmup, copies, cfg=2, kvd=None, graph=False):
+def run_decode_bench(steps, warmup, copies, workload="batch_decode", kvd=None, graph=False):
     import torch
 
     from attention_paged_fp8_amd import fi
-    from workloads import make_config
+    from workloads import make_workload
 
     dev = torch.device("cuda:0")
-    w = make_config(cfg, kvd=kvd)
+    w = make_workload(workload, kvd=kvd)
     q, idx, kvs, keep = _upload(w, dev, copies)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
@@ -188,10 +188,10 @@ def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False):
     import torch
 
     from attention_paged_fp8_amd import fi
-    from workloads import make_config, ragged_rows
+    from workloads import make_workload, ragged_rows
 
     dev = torch.device("cuda:0")
-    w = make_config(3, q="e4m3" if fp8q else None)
+    w = make_workload("causal_prefill", q="e4m3" if fp8q else None)
     q, idx, kvs, keep = _upload(w, dev, 0 if ragged else 1)
     o = torch.empty(q.shape, dtype=torch.float16, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
@@ -271,9 +271,10 @@ def decode_extra(steps, warmup):
     HIP-event medians and HBM rates (context beside the main line; each is a
     separate decode workload)."""
     out = {}
-    for key, cfg, kvd, copies in (("long_context", 4, None, 2), ("kv_f16", 5, "f16", 2), ("kv_bf16_mixed", 5, "bf16", 2),
-                                  ("kv_e4m3", 5, "e4m3", 4), ("kv_e4m3fnuz", 2, "e4m3fnuz", 4)):
-        w, wall_ms, ev = run_decode_bench(steps, warmup, copies, cfg=cfg, kvd=kvd)
+    for key, wl, kvd, copies in (("long_context", "long_context_decode", None, 2), ("kv_f16", "dtype_decode", "f16", 2),
+                                 ("kv_bf16_mixed", "dtype_decode", "bf16", 2), ("kv_e4m3", "dtype_decode", "e4m3", 4),
+                                 ("kv_e4m3fnuz", "batch_decode", "e4m3fnuz", 4)):
+        w, wall_ms, ev = run_decode_bench(steps, warmup, copies, workload=wl, kvd=kvd)
         nb = decode_bytes(w)
         med = float(np.median(ev))
         out[key] = {"workload": w["name"] + (f"_kv_{kvd}" if kvd else ""), "bytes_per_call": nb,
@@ -354,9 +355,9 @@ def main():
         from attention_paged_fp8_amd.build import build
         build()
 
-    from workloads import make_config
+    from workloads import make_workload
 
-    w, eager_ms, ev, graph_ms = make_config(2), float("nan"), np.array([float("nan")]), float("nan")
+    w, eager_ms, ev, graph_ms = make_workload("batch_decode"), float("nan"), np.array([float("nan")]), float("nan")
     if args.only in ("all", "decode"):
         w, eager_ms, ev, graph_ms = run_decode_bench(args.steps, args.warmup, args.copies, graph=True)
     nbytes = decode_bytes(w)

@@ -1,8 +1,8 @@
 """GPU parity tests for decode (batched paged, single) and the fp8 widening,
 through the C ABI, against the float64 oracle.
 
-Cases: every fp8 code widened bitwise; the measured configurations 1, 2, 4 and
-5 compared element by element at full size; a matrix of small shapes spanning
+Cases: every fp8 code widened bitwise; the measured single-decode, batch-decode,
+long-context and dtype-decode workloads compared element by element at full size; a matrix of small shapes spanning
 several 32-token blocks, ragged tails, empty and one-token requests, page
 sizes 1..128, head_dim 64 and 128, GQA groups 1..32, all q / KV / o dtype
 combinations decode admits (fnuz caches included), forced split-KV; and the invariants: run-to-run
@@ -21,7 +21,7 @@ import torch
 import oracle.attention as OA
 from oracle.fp8 import fp8_table
 from attention_paged_fp8_amd import fi
-from workloads import make_config, make_paged
+from workloads import make_paged, make_workload
 from gpu_util import (O_TOL, T2, assert_parity, dev_2byte, paged_kv, run_decode, say, upload, workspace_for)
 
 pytestmark = pytest.mark.gpu
@@ -47,15 +47,15 @@ def test_fp8_widen_all_codes_bitwise(gpu_device, src, dst):
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 stays -0
 
 
-# ------------------------------------------------------------------ config 1
-def test_config1_single_and_batch(gpu_device):
-    say("config1")
-    w = make_config(1)
+# ------------------------------------------------------------------ the single-decode workload
+def test_single_decode_single_and_batch(gpu_device):
+    say("single_decode")
+    w = make_workload("single_decode")
     d = upload(w, gpu_device)
     o_ref, l_ref = OA.batch_decode(w)
     o_b, l_b, _ = run_decode(w, d)
     assert_parity(o_b, l_b, o_ref, l_ref, "f16", "batch decode")
-    # single decode: contiguous K/V [kv_len, H, D] (pages are contiguous in config 1)
+    # single decode: contiguous K/V [kv_len, H, D] (pages are contiguous in the single-decode workload)
     kv_len = int(w["kv_lens"][0])
     k = d["k"].reshape(-1, w["num_kv_heads"], w["head_dim"])[:kv_len]
     v = d["v"].reshape(-1, w["num_kv_heads"], w["head_dim"])[:kv_len]
@@ -112,34 +112,34 @@ def test_decode_small(gpu_device, case):
             assert np.all(og[i] == 0) and np.all(np.isneginf(lg[i]))
 
 
-# ------------------------------------------------------------------ full-size configs
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_config_full_size(gpu_device, cfg):
-    say("config", cfg)
-    w = make_config(cfg)
+# ------------------------------------------------------------------ full-size workloads
+@pytest.mark.parametrize("wl", ["batch_decode", "long_context_decode"])
+def test_workload_full_size(gpu_device, wl):
+    say("workload", wl)
+    w = make_workload(wl)
     d = upload(w, gpu_device)
     og, lg, _ = run_decode(w, d)
     del d
     torch.cuda.empty_cache()
     o_ref, l_ref = OA.batch_decode(w)
-    err = assert_parity(og, lg, o_ref, l_ref, w["o_dtype"], f"config {cfg}")
-    print(f"config {cfg}: max |o - oracle| = {err:.3e}")
+    err = assert_parity(og, lg, o_ref, l_ref, w["o_dtype"], wl)
+    print(f"{wl}: max |o - oracle| = {err:.3e}")
 
 
 @pytest.mark.parametrize("kvd", ["f16", "bf16", "e4m3"])
-def test_config5_legs(gpu_device, kvd):
-    say("config5", kvd)
-    w = make_config(5, kvd=kvd)
+def test_dtype_decode_legs(gpu_device, kvd):
+    say("dtype_decode", kvd)
+    w = make_workload("dtype_decode", kvd=kvd)
     d = upload(w, gpu_device)
     og, lg, _ = run_decode(w, d)
     o_ref, l_ref = OA.batch_decode(w)
-    assert_parity(og, lg, o_ref, l_ref, "f16", f"config 5 {kvd}")
+    assert_parity(og, lg, o_ref, l_ref, "f16", f"dtype-decode workload {kvd}")
 
 
-def test_config5_refusals_with_real_tensors(gpu_device):
+def test_dtype_decode_refusals_with_real_tensors(gpu_device):
     """k/v dtype mismatch, integer KV and fp8 output must error, and leave o
     untouched."""
-    say("config5 refusals")
+    say("dtype_decode refusals")
     w = make_paged(5, kv_lens=[100, 40], hq=32, hkv=8, d=128, page=16, q="f16", kvd="e4m3")
     d = upload(w, gpu_device)
     o = torch.full((2, 32, 128), 7.0, dtype=torch.float16, device=gpu_device)
@@ -174,8 +174,8 @@ def test_fnuz_batch_decode_shapes_and_single(gpu_device, kvd):
     """The batch-decode shapes (64 requests of 512..4096 tokens, 32/8 heads,
     page 16 shuffled) over an fnuz cache, whole requests against the oracle;
     and fi_single_decode over one request's rows."""
-    say("fnuz config2 shapes", kvd)
-    w = make_config(2, kvd=kvd)
+    say("fnuz batch_decode shapes", kvd)
+    w = make_workload("batch_decode", kvd=kvd)
     d = upload(w, gpu_device)
     og, lg, _ = run_decode(w, d)
     reqs = [0, 17, 40, 63]

@@ -15,7 +15,7 @@ import torch
 
 import oracle.attention as OA
 from attention_paged_fp8_amd import fi
-from workloads import make_config
+from workloads import make_workload
 from gpu_util import T2, assert_parity, paged_kv, say, upload, workspace_for
 
 pytestmark = pytest.mark.gpu
@@ -45,10 +45,10 @@ def _capture(fn, stream):
     return g
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_decode_graph_replays(gpu_device, cfg):
-    say("graph decode config", cfg)
-    w = make_config(cfg)
+@pytest.mark.parametrize("wl", ["batch_decode", "long_context_decode"])
+def test_decode_graph_replays(gpu_device, wl):
+    say("graph decode", wl)
+    w = make_workload(wl)
     d = upload(w, gpu_device)
     kv, keep = paged_kv(w, d)
     B, H, D = len(w["kv_lens"]), w["num_qo_heads"], w["head_dim"]
@@ -81,16 +81,16 @@ def test_decode_graph_replays(gpu_device, cfg):
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {r}: output differs from eager"
         assert torch.equal(lse, l_e), f"replay {r}: lse differs from eager"
-        if r == 0 and cfg == 2:  # the long-context workload's full oracle is covered by the decode tests
+        if r == 0 and wl == "batch_decode":  # the long-context workload's full oracle is covered by the decode tests
             o_ref, l_ref = OA.batch_decode(w)
             assert_parity(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, w["o_dtype"],
-                          f"graph replay, config {cfg}")
+                          f"graph replay, {wl}")
     del g
 
 
 def test_prefill_graph_replays(gpu_device):
-    say("graph prefill config 3")
-    w = make_config(3)
+    say("graph prefill causal-prefill workload")
+    w = make_workload("causal_prefill")
     d = upload(w, gpu_device)
     kv, keep = paged_kv(w, d)
     T, H, D = int(w["qo_indptr"][-1]), w["num_qo_heads"], w["head_dim"]

@@ -1,7 +1,7 @@
 """GPU parity tests for batched paged prefill (causal and not), through the C
 ABI, against the float64 oracle.
 
-Cases: the causal prefill configuration (3) at full size -- four requests
+Cases: the causal-prefill workload (16 requests, qo 256..1024, prefix 0..2048, 32/8 heads, d 128) at full size -- four requests
 compared element by element and sampled rows of every request; a matrix of
 small shapes (GQA groups 1, 2, 3, 4, 8, 32; head_dim 64 and 128; page sizes 1 to
 128; fp8 and same-type 2-byte KV; causal and non-causal; ragged query and
@@ -19,7 +19,7 @@ import torch
 
 import oracle.attention as OA
 from oracle.fp8 import fp8_table
-from workloads import make_config, make_paged
+from workloads import make_paged, make_workload
 from gpu_util import T2, assert_parity, paged_kv, run_decode, run_prefill, say, upload
 
 pytestmark = pytest.mark.gpu
@@ -59,9 +59,9 @@ def test_prefill_small(gpu_device, case):
     assert_parity(og, lg, o_ref, l_ref, o, str(case))
 
 
-def test_config3_full_size(gpu_device):
-    say("config3")
-    w = make_config(3)
+def test_causal_prefill_full_size(gpu_device):
+    say("causal_prefill")
+    w = make_workload("causal_prefill")
     d = upload(w, gpu_device)
     og, lg, _ = run_prefill(w, d, causal=True)
     og2, lg2, _ = run_prefill(w, d, causal=True)
@@ -71,7 +71,7 @@ def test_config3_full_size(gpu_device):
     qi = w["qo_indptr"]
     for i in reqs:
         a, b = int(qi[i]), int(qi[i + 1])
-        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"config 3 request {i}")
+        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"causal-prefill workload request {i}")
     # sampled rows of every request: first, last and random rows, every head
     rng = np.random.default_rng(0)
     toks, heads = [], []
@@ -82,7 +82,7 @@ def test_config3_full_size(gpu_device):
                 toks.append(t)
                 heads.append(int(h))
     o_s, l_s = OA.attention_rows(w, toks, heads, causal=True)
-    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "config 3 sampled rows")
+    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "causal-prefill workload sampled rows")
 
 
 def test_rows_without_visible_keys(gpu_device):

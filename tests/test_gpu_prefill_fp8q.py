@@ -21,7 +21,7 @@ the exact mean of the visible V rows: that pins the pairing of P and V keys.
 
 Cases: both query formats against both cache formats, both output types,
 head_dim 64 and 128, GQA groups 1 to 8, page sizes 1 to 128, causal and not,
-ragged lengths that leave partial tiles; the causal prefill configuration (3)
+ragged lengths that leave partial tiles; the causal-prefill workload (16 requests, qo 256..1024, prefix 0..2048, 32/8 heads, d 128)
 with its query quantised to e4m3, at full size (whole requests and sampled
 rows); requests without queries or keys; run-to-run and page-permutation
 determinism (bitwise).
@@ -31,7 +31,7 @@ import pytest
 import torch
 
 import oracle.attention as OA
-from workloads import make_config, make_paged
+from workloads import make_paged, make_workload
 from gpu_util import LSE_TOL, O_TOL, T2, assert_parity, paged_kv, say, upload
 from attention_paged_fp8_amd import fi
 
@@ -74,15 +74,15 @@ def test_fp8q_small(gpu_device, case):
     assert_parity(og, lg, o_ref, l_ref, o, str(case))
 
 
-def _config3_fp8q():
-    """The causal prefill configuration (3) with its query quantised to e4m3
+def _causal_prefill_fp8q():
+    """The causal-prefill workload with its query quantised to e4m3
     (per-tensor scale): the same lengths, pages and draws."""
-    return make_config(3, q="e4m3")
+    return make_workload("causal_prefill", q="e4m3")
 
 
-def test_config3_fp8q_full_size(gpu_device):
-    say("config3 fp8q")
-    w = _config3_fp8q()
+def test_causal_prefill_fp8q_full_size(gpu_device):
+    say("causal_prefill fp8q")
+    w = _causal_prefill_fp8q()
     d = upload(w, gpu_device)
     og, lg = run_fp8q(w, d)
     og2, lg2 = run_fp8q(w, d)
@@ -92,7 +92,7 @@ def test_config3_fp8q_full_size(gpu_device):
     qi = w["qo_indptr"]
     for i in reqs:
         a, b = int(qi[i]), int(qi[i + 1])
-        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"config 3 fp8q request {i}")
+        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"causal-prefill workload fp8q request {i}")
     rng = np.random.default_rng(1)
     toks, heads = [], []
     for i in range(len(w["qo_lens"])):
@@ -102,7 +102,7 @@ def test_config3_fp8q_full_size(gpu_device):
                 toks.append(t)
                 heads.append(int(h))
     o_s, l_s = OA.attention_rows(w, toks, heads, causal=True)
-    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "config 3 fp8q sampled rows")
+    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "causal-prefill workload fp8q sampled rows")
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -206,11 +206,11 @@ def test_fp8q_pv8_zero_query_is_exact_mean(gpu_device, causal):
     assert_parity(og, lg, o_ref, l_ref, "f16", "zero query, fp8 P V")
 
 
-def test_config3_fp8q_pv8_sampled_rows(gpu_device):
-    """The causal prefill configuration (3), fp8 query, fp8 P V: sampled rows
+def test_causal_prefill_fp8q_pv8_sampled_rows(gpu_device):
+    """The causal-prefill workload, fp8 query, fp8 P V: sampled rows
     against the oracle within the rounding bound, lse at 1e-3."""
-    say("config3 fp8q pv8")
-    w = _config3_fp8q()
+    say("causal_prefill fp8q pv8")
+    w = _causal_prefill_fp8q()
     d = upload(w, gpu_device)
     og, lg = run_fp8q(w, d, pv_fp8=True)
     og2, lg2 = run_fp8q(w, d, pv_fp8=True)

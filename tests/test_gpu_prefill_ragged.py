@@ -14,7 +14,7 @@ layouts.  Here:
 * single-request prefill against the oracle and bitwise against that request
   inside a paged batch, including a request without keys;
 * ragged requests without queries or keys, and rows that see no key;
-* the causal prefill configuration (3) as a ragged batch, bitwise against the
+* the causal-prefill workload (16 requests, qo 256..1024, prefix 0..2048, 32/8 heads, d 128) as a ragged batch, bitwise against the
   paged call at full size.
 """
 import numpy as np
@@ -23,7 +23,7 @@ import torch
 
 import oracle.attention as OA
 from oracle.fp8 import fp8_table
-from workloads import make_config, make_paged, ragged_rows
+from workloads import make_paged, make_workload, ragged_rows
 from gpu_util import T2, assert_parity, dev_pool, run_prefill, say, upload
 from attention_paged_fp8_amd import fi
 
@@ -142,11 +142,11 @@ def test_single_prefill(gpu_device, case):
     assert np.array_equal(og, op) and np.array_equal(lg, lp), "single and paged calls differ"
 
 
-def test_config3_ragged_equals_paged(gpu_device):
-    """The causal prefill configuration (3) as a ragged batch: bitwise equal to
+def test_causal_prefill_ragged_equals_paged(gpu_device):
+    """The causal-prefill workload as a ragged batch: bitwise equal to
     the paged call, which the paged tests hold to the oracle."""
-    say("config3 ragged")
-    w = make_config(3)
+    say("causal_prefill ragged")
+    w = make_workload("causal_prefill")
     dv = upload(w, gpu_device)
     kv, keep = ragged_kv(w, gpu_device, lead=16)
     og, lg = run_ragged(w, dv, kv)
@@ -155,4 +155,4 @@ def test_config3_ragged_equals_paged(gpu_device):
     i = 3
     a, b = int(w["qo_indptr"][i]), int(w["qo_indptr"][i + 1])
     o_ref, l_ref = OA.batch_prefill(w, causal=True, requests=[i])
-    assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", "config 3 ragged request 3")
+    assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", "causal-prefill workload ragged request 3")

@@ -8,8 +8,8 @@ the library.
 
 Shapes follow the workloads of the pages: GQA 32 q heads / 8 kv heads,
 head_dim 128, page 16 ("fp8 KV cache in the in-tree prefill kernel",
-AMD-Ecosystem/flashinfer PR #368, Benchmark results), plus the configurations
-this library is measured on (``CONFIGS``).  Values are N(0, 1): the pages use
+AMD-Ecosystem/flashinfer PR #368, Benchmark results), plus the workloads
+this library is measured on (``WORKLOADS``, by name).  Values are N(0, 1): the pages use
 model activations but provide none, so standard normals stand in.
 
 Draw order for one workload (numpy default_rng(seed)):
@@ -45,18 +45,18 @@ _TORCH = {
 NAN_BITS = {"e4m3": 0x7F, "e5m2": 0x7F, "e4m3fnuz": 0x80, "e5m2fnuz": 0x80, "f16": 0x7E00, "bf16": 0x7FC0}
 ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e4m3fnuz": 1, "e5m2fnuz": 1}
 
-# The five measured configurations.
-CONFIGS = {
-    1: dict(name="single_decode_kv64_h4-4_d64_page16_e4m3_f16", kind="single_decode", batch=1,
+# The measured workloads, by name; each draws from its own fixed seed.
+WORKLOADS = {
+    "single_decode": dict(seed=1, name="single_decode_kv64_h4-4_d64_page16_e4m3_f16", kind="single_decode", batch=1,
             kv=(64, 64), hq=4, hkv=4, d=64, page=16, q="f16", kvd="e4m3", o="f16", contiguous=True),
-    2: dict(name="batch_decode_b64_kv512-4096_h32-8_d128_page16_e4m3_bf16", kind="decode", batch=64,
+    "batch_decode": dict(seed=2, name="batch_decode_b64_kv512-4096_h32-8_d128_page16_e4m3_bf16", kind="decode", batch=64,
             kv=(512, 4096), hq=32, hkv=8, d=128, page=16, q="bf16", kvd="e4m3", o="bf16", contiguous=False),
-    3: dict(name="causal_prefill_b16_qo256-1024_prefix0-2048_h32-8_d128_page16_e4m3_f16", kind="prefill",
+    "causal_prefill": dict(seed=3, name="causal_prefill_b16_qo256-1024_prefix0-2048_h32-8_d128_page16_e4m3_f16", kind="prefill",
             batch=16, qo=(256, 1024), prefix=(0, 2048), hq=32, hkv=8, d=128, page=16, q="f16", kvd="e4m3",
             o="f16", contiguous=False),
-    4: dict(name="splitkv_decode_b8_kv32768-131072_h64-8_d128_page64_e5m2_bf16", kind="decode", batch=8,
+    "long_context_decode": dict(seed=4, name="splitkv_decode_b8_kv32768-131072_h64-8_d128_page64_e5m2_bf16", kind="decode", batch=8,
             kv=(32768, 131072), hq=64, hkv=8, d=128, page=64, q="bf16", kvd="e5m2", o="bf16", contiguous=False),
-    5: dict(name="dtype_decode_b64_kv512-4096_h32-8_d128_page16_f16q", kind="decode", batch=64,
+    "dtype_decode": dict(seed=5, name="dtype_decode_b64_kv512-4096_h32-8_d128_page16_f16q", kind="decode", batch=64,
             kv=(512, 4096), hq=32, hkv=8, d=128, page=16, q="f16", kvd=("f16", "bf16", "e4m3"), o="f16",
             contiguous=False),
 }
@@ -172,20 +172,21 @@ def make_paged(seed: int, *, kv_lens=None, qo_lens=None, prefix_lens=None, hq: i
     )
 
 
-def make_config(cfg_id: int, kvd: str | None = None, q: str | None = None) -> dict:
-    """The workload of one measured configuration (seed = configuration number;
-    configuration 5 takes its KV dtype as an argument, one of f16, bf16, e4m3).
-    ``q`` replaces the query dtype (e.g. "e4m3": the same draws quantised with
-    a per-tensor scale); the name then says so."""
-    c = CONFIGS[cfg_id]
+def make_workload(key: str, kvd: str | None = None, q: str | None = None) -> dict:
+    """One measured workload by name (``WORKLOADS``); "dtype_decode" takes its
+    KV dtype as an argument, one of f16, bf16, e4m3 (default e4m3), and any
+    workload may be drawn with another KV dtype.  ``q`` replaces the query
+    dtype (e.g. "e4m3": the same draws quantised with a per-tensor scale); the
+    name then says so."""
+    c = WORKLOADS[key]
     kvd_eff = kvd if kvd is not None else (c["kvd"] if isinstance(c["kvd"], str) else c["kvd"][-1])
     common = dict(hq=c["hq"], hkv=c["hkv"], d=c["d"], page=c["page"], q=q or c["q"], kvd=kvd_eff, o=c["o"],
                   contiguous=c["contiguous"], batch=c["batch"])
     if c["kind"] == "prefill":
-        w = make_paged(cfg_id, qo_range=c["qo"], prefix_range=c["prefix"], **common)
+        w = make_paged(c["seed"], qo_range=c["qo"], prefix_range=c["prefix"], **common)
     else:
-        w = make_paged(cfg_id, kv_range=c["kv"], **common)
-    w["config"] = cfg_id
+        w = make_paged(c["seed"], kv_range=c["kv"], **common)
+    w["workload"] = key
     w["name"] = c["name"] + (f"_q{q}" if q else "")
     w["kind"] = c["kind"]
     return w
