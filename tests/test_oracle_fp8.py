@@ -114,3 +114,32 @@ def test_fnuz_specials():
         t = fp8.fp8_table(fmt)
         assert np.isnan(t[0x80]) and np.sum(np.isnan(t)) == 1 and np.all(np.isfinite(t[~np.isnan(t)]))
         assert not np.any(np.signbit(t[np.isfinite(t) & (t == 0)]))  # no negative zero
+
+
+def test_fnuz_codes_read_as_ocp():
+    """The format identities the decode kernel's fnuz widening rests on,
+    checked on all 256 codes of the oracle's tables.  e4m3fnuz (bias 8) read
+    as OCP e4m3 (bias 7) is exactly twice its value, except 0x7F / 0xFF (+-240,
+    an OCP NaN) and 0x80 (the fnuz NaN, OCP -0).  e5m2fnuz (bias 16) with its
+    exponent lowered by one, read as OCP e5m2 (bias 15), is its exact value
+    for every code with exponent >= 2 -- the top binade included -- while
+    exponents 0 and 1 fall outside that reading."""
+    e4_ocp, e4_fnuz = fp8.fp8_table("e4m3"), fp8.fp8_table("e4m3fnuz")
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            assert math.isnan(e4_ocp[c]) and abs(e4_fnuz[c]) == 240.0
+        elif c == 0x80:
+            assert math.isnan(e4_fnuz[c]) and e4_ocp[c] == 0.0 and math.copysign(1, e4_ocp[c]) < 0
+        else:
+            assert e4_ocp[c] == 2.0 * e4_fnuz[c], hex(c)
+    e5_ocp, e5_fnuz = fp8.fp8_table("e5m2"), fp8.fp8_table("e5m2fnuz")
+    for c in range(256):
+        e = (c >> 2) & 0x1F
+        if c == 0x80:
+            continue
+        if e >= 2:
+            assert e5_ocp[c - 4] == e5_fnuz[c], hex(c)
+        elif c & 0x7F:
+            # exponents 0 and 1: twice the value, not representable one binade lower
+            assert e5_ocp[c] == 2.0 * e5_fnuz[c], hex(c)
+    assert np.isinf(e5_ocp[0x7C]) and e5_fnuz[0x7C] == 32768.0  # the top binade is finite in fnuz
