@@ -86,9 +86,10 @@ __device__ __forceinline__ int request_kv_len(const DecodeParams& p, int b) {
 // scale by the host), widened exactly to fp16 as it is loaded; QBF16 is then
 // false and the kernel runs its fp16 path.
 template <bool QBF16, int KVF, bool OBF16, int D, int Q8 = 0>
-// (the e4m3fnuz form holds a step's codes in registers before widening them,
-// and is given the registers of two workgroups per CU)
-__global__ __launch_bounds__(256, KVF == FMT_E4M3_FNUZ ? 2 : FI_DECODE_MIN_WG_PER_CU) void decode_kernel(
+// (the fnuz forms hold a step's codes in registers before widening them, and
+// are given the registers of two workgroups per CU)
+__global__ __launch_bounds__(256, (KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) ? 2 : FI_DECODE_MIN_WG_PER_CU) void
+decode_kernel(
     const DecodeParams p) {
   using Cfg = DecodeCfg<QBF16, KVF, OBF16, D>;
   constexpr bool MB = Cfg::MBF16;
@@ -304,31 +305,42 @@ __global__ __launch_bounds__(256, KVF == FMT_E4M3_FNUZ ? 2 : FI_DECODE_MIN_WG_PE
       return [=](int u) { return *reinterpret_cast<const uint4*>(stage + k_off + 16 * ((kcol0 + u) ^ (c & swz))); };
     };
     auto compute = [&](int st, const uint8_t* stage) {
-      if constexpr (KVF == FMT_E4M3_FNUZ) {
-        // The step's codes are read first; unless one of them is +-240 (rare:
-        // the extremes of the tensor), the OCP converter widens them, else
-        // the exact bit form does -- the two give identical values.
+      if constexpr (KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) {
+        // The step's codes are read first; unless one of them lies outside
+        // the OCP reading (e4m3fnuz: +-240, the extremes of the tensor;
+        // e5m2fnuz: exponent 0 or 1, values below 2^-14 -- both rare), the
+        // OCP converter widens them, else the exact bit form does -- the two
+        // give identical values.
         constexpr int KU = Cfg::DL * Cfg::KVB / 16;
         uint4 kx[KU];
         uint2 vx[Cfg::NDB / 2];
+        auto outside = [](uint32_t w) {
+          if constexpr (KVF == FMT_E4M3_FNUZ)
+            return e4m3fnuz_maxcode(w);
+          else
+            return e5m2fnuz_low(w);
+        };
         uint32_t hit = 0;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
           kx[u] = k_lds(stage)(u);
-          hit |= e4m3fnuz_maxcode(kx[u].x) | e4m3fnuz_maxcode(kx[u].y) | e4m3fnuz_maxcode(kx[u].z) |
-                 e4m3fnuz_maxcode(kx[u].w);
+          hit |= outside(kx[u].x) | outside(kx[u].y) | outside(kx[u].z) | outside(kx[u].w);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NDB / 2; ++i) {
           vx[i] = lds_tr8(stage + v_off[i]);
-          hit |= e4m3fnuz_maxcode(vx[i].x) | e4m3fnuz_maxcode(vx[i].y);
+          hit |= outside(vx[i].x) | outside(vx[i].y);
         }
         auto kreg = [&](int u) { return kx[u]; };
         auto vreg = [&](int i) { return vx[i]; };
-        if (__builtin_amdgcn_ballot_w64(hit != 0) == 0)
-          compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e4m3fnuz_ocp<MB>(w); });
-        else
+        if (__builtin_amdgcn_ballot_w64(hit != 0) == 0) {
+          if constexpr (KVF == FMT_E4M3_FNUZ)
+            compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e4m3fnuz_ocp<MB>(w); });
+          else
+            compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e5m2fnuz_ocp<MB>(w); });
+        } else {
           compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4<MB, KVF>(w); });
+        }
       } else {
         compute_with(st, stage, k_lds(stage), [&](int i) { return lds_tr8(stage + v_off[i]); },
                      [](uint32_t w) { return widen4<MB, KVF>(w); });

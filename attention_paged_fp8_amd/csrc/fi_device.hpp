@@ -111,6 +111,33 @@ __device__ __forceinline__ uint32_t e4m3fnuz_maxcode(uint32_t w) {
   return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
 }
 
+// Fast form for e5m2fnuz: a code whose exponent field is 2 or more, with
+// that field lowered by one (4 subtracted from the byte), reads as OCP e5m2
+// (bias 15 against 16) with exactly the fnuz value -- the top binade, which
+// OCP keeps for inf/NaN, included; zero codes (0x00, and the NaN 0x80 that
+// reads as -0) stay as they are.  Codes with exponent 0 or 1 and a nonzero
+// magnitude (below 2^-14: tiny values) have no such reading; the caller
+// checks for them with e5m2fnuz_low first.
+__device__ __forceinline__ uint32_t e5m2fnuz_big(uint32_t w) {  // bit 7 of a byte: exponent >= 2
+  return ((w & 0x78787878u) + 0x78787878u) & 0x80808080u;
+}
+__device__ __forceinline__ uint32_t e5m2fnuz_low(uint32_t w) {  // bit 7 of a byte: exponent 0/1, nonzero
+  return ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & ~e5m2fnuz_big(w) & 0x80808080u;
+}
+template <bool QBF16>
+__device__ __forceinline__ uint2 widen4_e5m2fnuz_ocp(uint32_t w) {
+  const uint32_t x = w - (e5m2fnuz_big(w) >> 5);
+  uint2 r;
+  if constexpr (QBF16) {
+    r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x, 1.0f, false));
+    r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x, 1.0f, true));
+  } else {
+    r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x, 1.0f, false));
+    r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x, 1.0f, true));
+  }
+  return r;
+}
+
 // The two word_sel immediates must be compile-time constants.
 template <bool QBF16, int KVF>
 __device__ __forceinline__ uint2 widen4(uint32_t w) {

@@ -308,37 +308,48 @@ def test_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
 
 @pytest.mark.parametrize("plant", ["none", "some_steps"])
 @pytest.mark.parametrize("q", ["f16", "bf16"])
-def test_e4m3fnuz_extreme_codes(gpu_device, q, plant):
-    """e4m3fnuz decode widens through the OCP converter unless a wave's step
-    holds a +-240 code (0x7F / 0xFF), which OCP e4m3 reads as NaN; such steps
-    take the exact bit form.  With every extreme code removed (fast form
-    only) and with extremes planted in some steps of some requests (both
-    forms in one call), the output matches the oracle and is bit-identical to
-    the same values stored pre-widened in q's type."""
-    say("e4m3fnuz extremes", q, plant)
-    w = _mid_workload(kvd="e4m3fnuz", q=q)
+@pytest.mark.parametrize("kvd", ["e4m3fnuz", "e5m2fnuz"])
+def test_fnuz_outside_ocp_codes(gpu_device, kvd, q, plant):
+    """fnuz decode widens through the OCP converter unless a wave's step holds
+    a code with no OCP reading -- e4m3fnuz +-240 (0x7F / 0xFF, OCP NaN),
+    e5m2fnuz exponent 0 or 1 with a nonzero magnitude -- and such steps take
+    the exact bit form.  With every such code removed (fast form only) and
+    with some planted in every third step (both forms in one call), the
+    output matches the oracle and is bit-identical to the same values stored
+    pre-widened in q's type."""
+    say("fnuz outside-OCP codes", kvd, q, plant)
+    w = _mid_workload(kvd=kvd, q=q)
     kp, vp = w["k_pool"].copy(), w["v_pool"].copy()
     pages_of = lambda i: w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
     valid = np.zeros(kp.shape[:2], dtype=bool)  # (page, slot) holding a token of some request
     for i, n in enumerate(w["kv_lens"]):
         for t in range(int(n)):
             valid[pages_of(i)[t // 16], t % 16] = True
-    for pool in (kp, vp):  # drop the extremes already present: +-240 -> +-224
-        sel = valid[:, :, None, None] & ((pool == 0x7F) | (pool == 0xFF))
-        pool[sel] = pool[sel] - 1
+    vsel = valid[:, :, None, None]
+    if kvd == "e4m3fnuz":
+        outside = lambda pool: (pool == 0x7F) | (pool == 0xFF)
+        repl = lambda pool, sel: pool[sel] - 1  # +-240 -> +-224
+        planted = (0x7F, 0xFF)
+    else:
+        outside = lambda pool: ((pool & 0x78) == 0) & ((pool & 0x7F) != 0)
+        repl = lambda pool, sel: pool[sel] & 0x80  # tiny -> +-0
+        planted = (0x01, 0x06, 0x85, 0x87)
+    for pool in (kp, vp):
+        sel = vsel & outside(pool)
+        pool[sel] = repl(pool, sel)
     if plant == "some_steps":
         rng = np.random.default_rng(5)
         for i, n in enumerate(w["kv_lens"]):
             for t in range(0, int(n), 48):  # one token in every third 16-token step
                 pg, sl = pages_of(i)[t // 16], t % 16
                 h, dd = rng.integers(0, 8), rng.integers(0, 128)
-                (kp if (t // 48) % 2 == 0 else vp)[pg, sl, h, dd] = 0x7F if rng.integers(0, 2) else 0xFF
+                (kp if (t // 48) % 2 == 0 else vp)[pg, sl, h, dd] = planted[rng.integers(0, len(planted))]
     w = dict(w, k_pool=kp, v_pool=vp)
     d = upload(w, gpu_device)
     o1, l1, _ = run_decode(w, d)
     o_ref, l_ref = OA.batch_decode(w)
-    assert_parity(o1, l1, o_ref, l_ref, q, f"e4m3fnuz extremes {plant}")
-    tab = fp8_table("e4m3fnuz")
+    assert_parity(o1, l1, o_ref, l_ref, q, f"{kvd} outside-OCP codes {plant}")
+    tab = fp8_table(kvd)
     kw = tab[kp].astype(np.float32)
     vw = tab[vp].astype(np.float32)
     kw[~np.isfinite(kw)] = np.nan
