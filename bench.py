@@ -23,8 +23,8 @@ MFMA TFLOP/s at 4 * head_dim flops per visible (query, key) pair per q head,
 and the same workload with its K/V stored contiguously per request through
 the ragged call; beside them the long-context split-KV decode (8 requests of 32k..128k tokens,
 64/8 heads, page 64, e5m2) and the batch-decode shapes with f16 q/o over f16,
-bf16 (mixed 2-byte) and e4m3 caches, the batch-decode workload over an e4m3fnuz
-cache, a plain device copy's bandwidth for
+bf16 (mixed 2-byte) and e4m3 caches, the batch-decode workload over e4m3fnuz and
+e5m2fnuz caches, a plain device copy's bandwidth for
 context, and the float64 oracle timed on the host cores on a bounded sample.
 Roofline figures use the median of the per-call HIP events.
 """
@@ -273,7 +273,8 @@ def decode_extra(steps, warmup):
     out = {}
     for key, wl, kvd, copies in (("long_context", "long_context_decode", None, 2), ("kv_f16", "dtype_decode", "f16", 2),
                                  ("kv_bf16_mixed", "dtype_decode", "bf16", 2), ("kv_e4m3", "dtype_decode", "e4m3", 4),
-                                 ("kv_e4m3fnuz", "batch_decode", "e4m3fnuz", 4)):
+                                 ("kv_e4m3fnuz", "batch_decode", "e4m3fnuz", 4),
+                                 ("kv_e5m2fnuz", "batch_decode", "e5m2fnuz", 4)):
         w, wall_ms, ev = run_decode_bench(steps, warmup, copies, workload=wl, kvd=kvd)
         nb = decode_bytes(w)
         med = float(np.median(ev))
