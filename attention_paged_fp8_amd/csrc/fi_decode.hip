@@ -314,12 +314,7 @@ decode_kernel(
         constexpr int KU = Cfg::DL * Cfg::KVB / 16;
         uint4 kx[KU];
         uint2 vx[Cfg::NDB / 2];
-        auto outside = [](uint32_t w) {
-          if constexpr (KVF == FMT_E4M3_FNUZ)
-            return e4m3fnuz_maxcode(w);
-          else
-            return e5m2fnuz_low(w);
-        };
+        auto outside = [](uint32_t w) { return fnuz_outside_ocp<KVF>(w); };
         uint32_t hit = 0;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
@@ -333,14 +328,10 @@ decode_kernel(
         }
         auto kreg = [&](int u) { return kx[u]; };
         auto vreg = [&](int i) { return vx[i]; };
-        if (__builtin_amdgcn_ballot_w64(hit != 0) == 0) {
-          if constexpr (KVF == FMT_E4M3_FNUZ)
-            compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e4m3fnuz_ocp<MB>(w); });
-          else
-            compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_e5m2fnuz_ocp<MB>(w); });
-        } else {
+        if (__builtin_amdgcn_ballot_w64(hit != 0) == 0)
+          compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4_fnuz_ocp<MB, KVF>(w); });
+        else
           compute_with(st, stage, kreg, vreg, [](uint32_t w) { return widen4<MB, KVF>(w); });
-        }
       } else {
         compute_with(st, stage, k_lds(stage), [&](int i) { return lds_tr8(stage + v_off[i]); },
                      [](uint32_t w) { return widen4<MB, KVF>(w); });

@@ -138,6 +138,23 @@ __device__ __forceinline__ uint2 widen4_e5m2fnuz_ocp(uint32_t w) {
   return r;
 }
 
+// Either fnuz format: the test for codes outside the OCP reading, and the
+// fast widening valid for all other codes.
+template <int KVF>
+__device__ __forceinline__ uint32_t fnuz_outside_ocp(uint32_t w) {
+  if constexpr (KVF == FMT_E4M3_FNUZ)
+    return e4m3fnuz_maxcode(w);
+  else
+    return e5m2fnuz_low(w);
+}
+template <bool QBF16, int KVF>
+__device__ __forceinline__ uint2 widen4_fnuz_ocp(uint32_t w) {
+  if constexpr (KVF == FMT_E4M3_FNUZ)
+    return widen4_e4m3fnuz_ocp<QBF16>(w);
+  else
+    return widen4_e5m2fnuz_ocp<QBF16>(w);
+}
+
 // The two word_sel immediates must be compile-time constants.
 template <bool QBF16, int KVF>
 __device__ __forceinline__ uint2 widen4(uint32_t w) {

@@ -309,7 +309,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   // v8_row(t), which lists each 16-token block as tokens 0-3, 8-11, 4-7,
   // 12-15, so that every transposed read of P V takes 8 consecutive rows)
   auto v8_row = [](int t) { return (t & ~15) | (t & 3) | (((t >> 3) & 1) << 2) | (((t >> 2) & 1) << 3); };
-  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw, auto vperm) {
+  auto store_rows_with = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw, auto vperm, auto w4) {
+    auto w8 = [&](uint32_t lo, uint32_t hi) {
+      const uint2 a = w4(lo), b = w4(hi);
+      return make_uint4(a.x, a.y, b.x, b.y);
+    };
 #pragma unroll
     for (int j = 0; j < Cfg::PER; ++j) {
       if (!ld_on(j)) continue;
@@ -317,11 +321,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
       if constexpr (decltype(raw)::value) {
         *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = r[j];
       } else if constexpr (Cfg::kFp8) {  // dimensions 16c..16c+7 to position 8c, 16c+8.. to D/2 + 8c
-        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].x, r[j].y);
-        *reinterpret_cast<uint4*>(d + D + 16 * ld_col[j]) = widen8<QBF16, KVF>(r[j].z, r[j].w);
+        *reinterpret_cast<uint4*>(d + 16 * ld_col[j]) = w8(r[j].x, r[j].y);
+        *reinterpret_cast<uint4*>(d + D + 16 * ld_col[j]) = w8(r[j].z, r[j].w);
       } else {  // dimensions 8c..8c+7 to position 8(c/2) (c even) or D/2 + 8(c/2) (c odd)
         *reinterpret_cast<uint4*>(d + 16 * (ld_col[j] >> 1) + D * (ld_col[j] & 1)) = r[j];
       }
+    }
+  };
+  // fnuz caches widen through the OCP converter (fast form) unless a code of
+  // the wave's chunks lies outside the OCP reading; the two forms give
+  // identical values
+  auto store_rows = [&](const uint4(&r)[Cfg::PER], uint8_t* slot, int pitch, auto raw, auto vperm) {
+    auto exact = [](uint32_t w) { return widen4<QBF16, KVF>(w); };
+    if constexpr ((KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) && !decltype(raw)::value) {
+      uint32_t out = 0;
+#pragma unroll
+      for (int j = 0; j < Cfg::PER; ++j)
+        if (ld_on(j))
+          out |= fnuz_outside_ocp<KVF>(r[j].x) | fnuz_outside_ocp<KVF>(r[j].y) | fnuz_outside_ocp<KVF>(r[j].z) |
+                 fnuz_outside_ocp<KVF>(r[j].w);
+      if (__builtin_amdgcn_ballot_w64(out != 0) == 0)
+        store_rows_with(r, slot, pitch, raw, vperm, [](uint32_t w) { return widen4_fnuz_ocp<QBF16, KVF>(w); });
+      else
+        store_rows_with(r, slot, pitch, raw, vperm, exact);
+    } else {
+      store_rows_with(r, slot, pitch, raw, vperm, exact);
     }
   };
   auto store_k = [&](const Fetch& f, uint8_t* slot) {

@@ -148,6 +148,55 @@ def test_prefill_fp8_equals_prewidened_bitwise(gpu_device, kvd, q):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("plant", ["none", "some_tiles"])
+@pytest.mark.parametrize("kvd,q", [("e4m3fnuz", "bf16"), ("e4m3fnuz", "f16"), ("e5m2fnuz", "bf16"), ("e5m2fnuz", "f16")])
+def test_prefill_fnuz_outside_ocp_codes(gpu_device, kvd, q, plant):
+    """fnuz prefill widens a wave's K or V tile through the OCP converter
+    unless the tile holds a code with no OCP reading (e4m3fnuz +-240,
+    e5m2fnuz exponent 0 or 1 with a nonzero magnitude); such tiles take the
+    exact bit form.  With every such code removed (fast form only) and with
+    some planted every 160 tokens (both forms in one call), the output matches
+    the oracle and is bit-identical to the same values stored pre-widened."""
+    say("prefill fnuz outside-OCP codes", kvd, q, plant)
+    w = _prefill_mid(kvd=kvd, q=q)
+    kp, vp = w["k_pool"].copy(), w["v_pool"].copy()
+    pages_of = lambda i: w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
+    valid = np.zeros(kp.shape[:2], dtype=bool)  # (page, slot) holding a token of some request
+    for i, n in enumerate(w["kv_lens"]):
+        for t in range(int(n)):
+            valid[pages_of(i)[t // 16], t % 16] = True
+    vsel = valid[:, :, None, None]
+    if kvd == "e4m3fnuz":
+        outside = lambda pool: (pool == 0x7F) | (pool == 0xFF)
+        repl = lambda pool, sel: pool[sel] - 1  # +-240 -> +-224
+        planted = (0x7F, 0xFF)
+    else:
+        outside = lambda pool: ((pool & 0x78) == 0) & ((pool & 0x7F) != 0)
+        repl = lambda pool, sel: pool[sel] & 0x80  # tiny -> +-0
+        planted = (0x01, 0x06, 0x85, 0x87)
+    for pool in (kp, vp):
+        sel = vsel & outside(pool)
+        pool[sel] = repl(pool, sel)
+    if plant == "some_tiles":
+        rng = np.random.default_rng(6)
+        for i, n in enumerate(w["kv_lens"]):
+            for t in range(5, int(n), 160):
+                pg, sl = pages_of(i)[t // 16], t % 16
+                h, dd = rng.integers(0, 8), rng.integers(0, 128)
+                (kp if (t // 160) % 2 == 0 else vp)[pg, sl, h, dd] = planted[rng.integers(0, len(planted))]
+    w = dict(w, k_pool=kp, v_pool=vp)
+    d = upload(w, gpu_device)
+    o1, l1, _ = run_prefill(w, d, causal=True)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert_parity(o1, l1, o_ref, l_ref, w["o_dtype"], f"prefill {kvd} outside-OCP codes {plant}")
+    tab = fp8_table(kvd)
+    k2 = torch.from_numpy(tab[kp].astype(np.float32)).to(T2[q]).to(gpu_device)
+    v2 = torch.from_numpy(tab[vp].astype(np.float32)).to(T2[q]).to(gpu_device)
+    kv, keep = paged_kv(w, d, k=k2, v=v2, kv_dtype=q)
+    o2, l2, _ = run_prefill(w, d, causal=True, kv=kv)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_prefill_constant_v(gpu_device):
     """Every token carries the same V row: each output row is that row times
     v_scale (up to the output rounding), causal mask or not."""
