@@ -176,7 +176,10 @@ decode_kernel(
       for (int j = 0; j < Cfg::PER; ++j) {
         const int t = min(t_begin + st * kDecodeStep + ld_row[j], t_end - 1);
         const int pid = pids_s[(t >> shift) - pg_lo];
-        const int64_t off = (int64_t)pid * p.sp + (int64_t)(t & (p.page_size - 1)) * p.st + ld_off[j];
+        // byte strides are below 4 GiB and page ids and slots are non-negative:
+        // two 32 x 32 -> 64-bit multiply-adds instead of full 64-bit products
+        const uint64_t off = (uint64_t)(uint32_t)pid * (uint32_t)p.sp +
+                             ((uint64_t)(uint32_t)(t & (p.page_size - 1)) * (uint32_t)p.st + (uint64_t)ld_off[j]);
         r.k[j] = load16_stream(p.k + off);
         r.v[j] = load16_stream(p.v + off);
       }
