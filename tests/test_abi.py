@@ -332,6 +332,28 @@ def test_argument_refusals(L):
 
 
 @no_gpu
+def test_stride_limits(L):
+    """Byte strides are positive and below 4 GiB (the kernels form gather
+    offsets with 32 x 32 -> 64-bit products), for the paged and ragged calls."""
+    fake = 0x10000
+    kv, keep = _kv(ptrs=True)
+    kv.stride_page = 1 << 32  # fp8: one byte per element
+    assert _decode(L, kv, qp=fake, op=fake) == 2 and "below 4 GiB" in _err(L)
+    kv, keep = _kv(ptrs=True, k_dtype="f16")
+    kv.stride_token = 1 << 31  # 2 bytes per element: 4 GiB
+    assert _decode(L, kv, qp=fake, op=fake) == 2 and "below 4 GiB" in _err(L)
+    kv, keep = _kv(ptrs=True)
+    kv.stride_head = 0
+    assert _decode(L, kv, qp=fake, op=fake) == 2 and "strides must be positive" in _err(L)
+    kv, keep = _kv(ptrs=True)
+    kv.stride_page = (1 << 32) - 16  # the largest aligned stride passes every check; the launch then finds no GPU
+    assert _decode(L, kv, qp=fake, op=fake) == 5 and "no ROCm-capable device" in _err(L)
+    kv, keep = _ragged(ptrs=True)
+    kv.stride_head = 1 << 32
+    assert _prefill_ragged(L, kv, qp=fake, op=fake, qo_dev=fake) == 2 and "below 4 GiB" in _err(L)
+
+
+@no_gpu
 def test_ragged_and_single_prefill_refusals(L):
     fake = 0x10000
     kv, keep = _ragged()
