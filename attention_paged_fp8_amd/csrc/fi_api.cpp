@@ -193,6 +193,9 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 #define FI_DECODE_TARGET_WG 2048
 #endif
 constexpr int kMinAutoChunk = FI_DECODE_MIN_CHUNK;  // smallest chunk the planner picks by itself
+#ifndef FI_DECODE_INTERLEAVE
+#define FI_DECODE_INTERLEAVE 1
+#endif
 constexpr int kTargetWorkgroups = FI_DECODE_TARGET_WG;  // workgroups the planner aims for
 
 // Split-KV plan: tokens per chunk (a multiple of kChunkQuantum); a chunk that
@@ -280,7 +283,17 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
         p.pre[batch] = (int32_t)run;
         p.pre_n = batch + 1;
       }
-      p.n_wg = (int32_t)ceil_div(W, slice);
+      p.spg = 0;
+      if (FI_DECODE_INTERLEAVE && groups > 1) {
+        // every group cut into the same token slices (a few more workgroups than
+        // the group-major cut at most: widen the slice until they fit the slots)
+        while (groups * ceil_div(total_kv, slice) > slots && slice < total_kv) slice += fi::kDecodeStep;
+        p.slice = slice;
+        p.spg = (int32_t)ceil_div(total_kv, slice);
+        p.n_wg = (int32_t)(groups * p.spg);
+      } else {
+        p.n_wg = (int32_t)ceil_div(W, slice);
+      }
       p.max_chunks = (int32_t)(ceil_div(std::max<int64_t>(max_kv, 1), slice) + 1);
       p.chunk = 0;
       // a merge is needed if some (request, group) segment spans several slices
@@ -288,7 +301,7 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
       for (int32_t i = 0; i < batch && !merge; ++i) {
         const int64_t len = kv_of(i);
         for (int64_t gi = 0; gi < groups && len > 0; ++gi) {
-          const int64_t s0 = gi * total_kv + pre, s1 = s0 + len;
+          const int64_t s0 = (p.spg ? 0 : gi * total_kv) + pre, s1 = s0 + len;
           if (s0 / slice != (s1 - 1) / slice) {
             merge = true;
             break;

@@ -468,6 +468,30 @@ decode_kernel(
     for (int i = blockIdx.x; i < p.batch; i += gridDim.x)
       if (pre(i + 1) == pre(i))
         for (int k = tid; k < groups; k += 256) p.nch[(int64_t)i * groups + k] = 0;
+  if (p.spg > 0) {
+    // Interleaved: each group's T tokens are cut into spg slices of its own and
+    // workgroup w takes group w % groups, slice w / groups, so the workgroups
+    // that read one token's kv head groups (its row's parts) run side by side.
+    const int g = (int)(blockIdx.x % groups);
+    const int sl = (int)(blockIdx.x / groups);
+    int64_t t0 = (int64_t)sl * p.slice;
+    const int64_t t1 = min(T, t0 + p.slice);
+    while (t0 < t1) {
+      int lo = 0, hi = p.batch;  // largest b with pre[b] <= t0
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre(mid) <= t0) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int64_t seg0 = pre(b), seg1 = pre(b + 1);
+      const int64_t end = min(seg1, t1);
+      const int64_t s_first = seg0 / p.slice;
+      const int nchunks = (int)((seg1 - 1) / p.slice - s_first + 1);
+      process(b, g, (int)(t0 - seg0), (int)(end - seg0), (int)(sl - s_first), nchunks);
+      t0 = end;
+    }
+    return;
+  }
   int64_t x0 = (int64_t)blockIdx.x * p.slice;
   const int64_t x1 = min(W, x0 + p.slice);
   while (x0 < x1) {

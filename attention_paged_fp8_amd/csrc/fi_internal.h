@@ -45,6 +45,8 @@ struct DecodeParams {
   int32_t balanced;       // 1: equal slices of the (group, request, token) space
   int32_t n_wg;           // balanced: workgroups launched
   int64_t slice;          // balanced: (group x token) items per workgroup
+  int32_t spg;            // balanced, interleaved: token slices per group (workgroup w: group w % groups,
+                          // slice w / groups); 0: slices of the group-major item space
   int32_t* nch;           // [batch, groups] pieces per segment, written for the merge (or null)
   float scale_log2;       // sm_scale * k_scale * log2(e)
   float v_scale;
