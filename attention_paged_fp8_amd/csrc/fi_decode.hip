@@ -387,8 +387,10 @@ decode_kernel(
     lr_run = xor_sum(lr_run, 16);
     lr_run = xor_sum(lr_run, 32);
     if (!row_ok) return;
-    const float inv = (lr_run > 0.f) ? 1.f / lr_run : 0.f;
-    const float lse2 = (l_run > 0.f) ? m_run + fast_log2(l_run) : kNegInf;
+    // a row without keys has sums of exactly 0; a NaN read from the cache
+    // makes them NaN, which then carries into o and lse
+    const float inv = (lr_run != 0.f) ? 1.f / lr_run : 0.f;
+    const float lse2 = (l_run != 0.f) ? m_run + fast_log2(l_run) : kNegInf;
     if (nchunks == 1) {
       const float f = inv * p.v_scale;
       uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + h) * D + 4 * qg;
@@ -581,10 +583,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const MergePara
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-  const float f = (L > 0.f) ? p.v_scale / L : 0.f;
+  // L is 0 only when every piece is empty; a NaN partial makes it NaN
+  const float f = (L != 0.f) ? p.v_scale / L : 0.f;
   if constexpr (PL == 2) *reinterpret_cast<uint32_t*>(op) = pack2<OBF16>(acc[0] * f, acc[1] * f);
   else *op = to_bits<OBF16>(acc[0] * f);
-  if (lsep && lane == 0) *lsep = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  if (lsep && lane == 0) *lsep = (L != 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------

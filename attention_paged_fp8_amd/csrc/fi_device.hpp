@@ -57,21 +57,29 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 //    in the integer domain -- one exponent step down for exponent >= 2, a
 //    right shift below, i.e. max(sat(mag - 0x400), mag >> 1) -- gives the
 //    value exactly, the top binade 2^15 .. 57344 included.
-// The NaN code 0x80 reads as -0 (a cache holds it only as a NaN).
-// bf16 is then reached from fp16 exactly (every fnuz value has at most 4
-// significant bits and lies within fp16's range).
+// The NaN code 0x80 (sign set, magnitude zero: the format's only NaN) gives a
+// half of exactly 0x8000 after the shifts above; it is turned into the quiet
+// NaN 0xFE00, so a NaN stored in an fnuz cache propagates as it does from an
+// OCP one.  bf16 is then reached from fp16 exactly (every fnuz value has at
+// most 4 significant bits and lies within fp16's range; NaN stays NaN).
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 template <int KVF>
 __device__ __forceinline__ uint32_t fnuz2_f16(uint32_t x) {
+  uint32_t r;
   if constexpr (KVF == FMT_E4M3_FNUZ) {
-    return ((x >> 1) & 0x3F803F80u) | (x & 0x80008000u);
+    r = ((x >> 1) & 0x3F803F80u) | (x & 0x80008000u);
   } else {
     const u16x2_t mag = bitcast<u16x2_t>(x & 0x7F007F00u);
     const u16x2_t step = {0x0400, 0x0400};
-    const u16x2_t r = __builtin_elementwise_max(__builtin_elementwise_sub_sat(mag, step), mag >> (unsigned short)1);
-    return bitcast<uint32_t>(r) | (x & 0x80008000u);
+    const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_sub_sat(mag, step), mag >> (unsigned short)1);
+    r = bitcast<uint32_t>(m) | (x & 0x80008000u);
   }
+  // the NaN code: a half equal to 0x8000 becomes 0xFE00
+  const u16x2_t h = bitcast<u16x2_t>(r);
+  const u16x2_t eq = __builtin_convertvector(h == (unsigned short)0x8000, u16x2_t);  // all ones where equal
+  const u16x2_t nan_bits = {0x7E00, 0x7E00};
+  return r | bitcast<uint32_t>(eq & nan_bits);
 }
 
 template <bool QBF16, int KVF>
@@ -88,10 +96,10 @@ __device__ __forceinline__ uint2 fnuz4(uint32_t w) {
 }
 
 // Fast form for e4m3fnuz: apart from 0x7F / 0xFF (+-240, which OCP e4m3
-// reads as NaN) the same bits read as OCP e4m3 are exactly twice the fnuz
-// value (bias 7 against 8; 0x80 reads as -0 either way), so the OCP converter
-// with scale 2^-8 gives value * 2^-7 -- bit for bit what fnuz4 builds.  The
-// caller checks its codes with e4m3fnuz_maxcode first.
+// reads as NaN) and the NaN code 0x80 (which OCP reads as -0) the same bits
+// read as OCP e4m3 are exactly twice the fnuz value (bias 7 against 8), so
+// the OCP converter with scale 2^-8 gives value * 2^-7 -- bit for bit what
+// fnuz4 builds.  The caller checks its codes with e4m3fnuz_outside first.
 template <bool QBF16>
 __device__ __forceinline__ uint2 widen4_e4m3fnuz_ocp(uint32_t w) {
   constexpr float k = 0.00390625f;  // 2^-8
@@ -105,24 +113,30 @@ __device__ __forceinline__ uint2 widen4_e4m3fnuz_ocp(uint32_t w) {
   }
   return r;
 }
-// Bit 7 of byte i of the result is set iff byte i of w is 0x7F or 0xFF (its
-// low 7 bits all ones: adding 1 carries into bit 7, and no byte carries out).
-__device__ __forceinline__ uint32_t e4m3fnuz_maxcode(uint32_t w) {
-  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+// Bit 7 of byte i of the result is set iff byte i of w is 0x7F, 0xFF or 0x80.
+// With m = the low 7 bits of each byte (no byte carries out of the sums
+// below): m + 1 reaches bit 7 iff m is all ones (+-240); m + 0x7F reaches bit
+// 7 iff m is nonzero, so a set sign bit without it is the NaN code.
+__device__ __forceinline__ uint32_t e4m3fnuz_outside(uint32_t w) {
+  const uint32_t m = w & 0x7F7F7F7Fu;
+  return ((m + 0x01010101u) | (w & ~(m + 0x7F7F7F7Fu))) & 0x80808080u;
 }
 
 // Fast form for e5m2fnuz: a code whose exponent field is 2 or more, with
 // that field lowered by one (4 subtracted from the byte), reads as OCP e5m2
 // (bias 15 against 16) with exactly the fnuz value -- the top binade, which
-// OCP keeps for inf/NaN, included; zero codes (0x00, and the NaN 0x80 that
-// reads as -0) stay as they are.  Codes with exponent 0 or 1 and a nonzero
-// magnitude (below 2^-14: tiny values) have no such reading; the caller
-// checks for them with e5m2fnuz_low first.
+// OCP keeps for inf/NaN, included; the zero code 0x00 stays as it is.  Codes
+// with exponent 0 or 1 and a nonzero magnitude (below 2^-14: tiny values)
+// have no such reading, nor has the NaN code 0x80 (OCP reads it as -0); the
+// caller checks for them with e5m2fnuz_outside first.
 __device__ __forceinline__ uint32_t e5m2fnuz_big(uint32_t w) {  // bit 7 of a byte: exponent >= 2
   return ((w & 0x78787878u) + 0x78787878u) & 0x80808080u;
 }
-__device__ __forceinline__ uint32_t e5m2fnuz_low(uint32_t w) {  // bit 7 of a byte: exponent 0/1, nonzero
-  return ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & ~e5m2fnuz_big(w) & 0x80808080u;
+// bit 7 of a byte: a nonzero magnitude with exponent 0/1, or the NaN code
+// (magnitude zero, sign set) -- per byte, nonzero ? !big : sign
+__device__ __forceinline__ uint32_t e5m2fnuz_outside(uint32_t w) {
+  const uint32_t nz = (w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+  return ((nz & ~e5m2fnuz_big(w)) | (~nz & w)) & 0x80808080u;
 }
 template <bool QBF16>
 __device__ __forceinline__ uint2 widen4_e5m2fnuz_ocp(uint32_t w) {
@@ -143,9 +157,9 @@ __device__ __forceinline__ uint2 widen4_e5m2fnuz_ocp(uint32_t w) {
 template <int KVF>
 __device__ __forceinline__ uint32_t fnuz_outside_ocp(uint32_t w) {
   if constexpr (KVF == FMT_E4M3_FNUZ)
-    return e4m3fnuz_maxcode(w);
+    return e4m3fnuz_outside(w);
   else
-    return e5m2fnuz_low(w);
+    return e5m2fnuz_outside(w);
 }
 template <bool QBF16, int KVF>
 __device__ __forceinline__ uint2 widen4_fnuz_ocp(uint32_t w) {

@@ -285,8 +285,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void prefill_kernel(const Pr
   };
   auto offset = [&](int tile, int j, uint32_t pid) -> uint64_t {
     if (RAGGED) return (uint64_t)pid * (uint32_t)p.st + (uint32_t)(ld_col[j] * 16);
+    // byte strides are below 4 GiB, page ids and slots non-negative: each term
+    // is a 32 x 32 -> 64-bit product (a slot times the token stride can pass
+    // 4 GiB, e.g. 127 slots of a token-major pool)
     const int t = row_token(tile, j);
-    return (uint64_t)pid * (uint32_t)p.sp + (uint32_t)((t & (p.page_size - 1)) * (uint32_t)p.st) +
+    return (uint64_t)pid * (uint32_t)p.sp + (uint64_t)(uint32_t)(t & (p.page_size - 1)) * (uint32_t)p.st +
            (uint32_t)(ld_col[j] * 16);
   };
   auto locate = [&](int tile, const uint32_t(&pid)[Cfg::PER]) {

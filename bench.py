@@ -185,11 +185,14 @@ def run_decode_bench(steps, warmup, copies, workload="batch_decode", kvd=None, g
     return w, wall_ms, ev
 
 
-def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False):
+def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False, copies=3):
     """The causal prefill workload through the paged call, or (ragged) the
     same K/V values stored contiguously per request through the ragged call,
     or (fp8q) with its query quantised to e4m3 through the fp8-query call
-    (pv_fp8: P V on the fp8 MFMA as well)."""
+    (pv_fp8: P V on the fp8 MFMA as well).  One call reads about 220 MB (q,
+    K/V, o), less than the 256 MB last-level cache, so `copies` full sets of
+    q, K/V, o and lse are rotated across the steps and no step finds the
+    previous step's lines in that cache."""
     import torch
 
     from attention_paged_fp8_amd import fi
@@ -197,30 +200,38 @@ def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False):
 
     dev = torch.device("cuda:0")
     w = make_workload("causal_prefill", q="e4m3" if fp8q else None)
-    q, idx, kvs, keep = _upload(w, dev, 0 if ragged else 1)
-    o = torch.empty(q.shape, dtype=torch.float16, device=dev)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    if ragged:
-        kr, vr, indptr = ragged_rows(w)
-        k, v = torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev)
-        ind = torch.from_numpy(indptr).to(dev)
-        rkv, rkeep = fi.make_ragged_kv(k, v, ind, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=w["kv_dtype"],
-                                       indptr_h=indptr)
+    sets = []
+    for _ in range(copies):
+        q, idx, kvs, keep = _upload(w, dev, 0 if ragged else 1)
+        o = torch.empty(q.shape, dtype=torch.float16, device=dev)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        kv = kvs[0] if kvs else None
+        if ragged:
+            kr, vr, indptr = ragged_rows(w)
+            k, v = torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev)
+            ind = torch.from_numpy(indptr).to(dev)
+            kv, rkeep = fi.make_ragged_kv(k, v, ind, k_scale=w["k_scale"], v_scale=w["v_scale"],
+                                          kv_dtype=w["kv_dtype"], indptr_h=indptr)
+            keep = (keep, k, v, ind, rkeep)
+        sets.append((q, idx, kv, o, lse, keep))
 
     def step(i):
+        q, idx, kv, o, lse, _ = sets[i % copies]
         if fp8q:
-            fi.fi_batch_prefill_paged_fp8q(q, idx["qo_indptr"], kvs[0], o, q_dtype="e4m3", q_scale=w["q_scale"],
+            fi.fi_batch_prefill_paged_fp8q(q, idx["qo_indptr"], kv, o, q_dtype="e4m3", q_scale=w["q_scale"],
                                            o_dtype=w["o_dtype"], causal=True, pv_fp8=pv_fp8, lse=lse,
                                            qo_indptr_h=w["qo_indptr"], stream=stream)
         elif ragged:
-            fi.fi_batch_prefill_ragged(q, idx["qo_indptr"], rkv, o, causal=True, lse=lse,
+            fi.fi_batch_prefill_ragged(q, idx["qo_indptr"], kv, o, causal=True, lse=lse,
                                        qo_indptr_h=w["qo_indptr"], stream=stream)
         else:
-            fi.fi_batch_prefill_paged(q, idx["qo_indptr"], kvs[0], o, causal=True, lse=lse,
+            fi.fi_batch_prefill_paged(q, idx["qo_indptr"], kv, o, causal=True, lse=lse,
                                       qo_indptr_h=w["qo_indptr"], stream=stream)
 
-    wall_ms, ev = _time_calls(step, 1, steps, warmup, stream)
+    wall_ms, ev = _time_calls(step, copies, steps, warmup, stream)
+    del sets
+    torch.cuda.empty_cache()
     return w, wall_ms, ev
 
 
@@ -307,30 +318,79 @@ def run_copy_calibration(mb: int, reps: int = 5):
     print(f"# copy calibration: {reps} copies of {n} bytes", flush=True)
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """The float64 oracle on a bounded sample of the decode workload: whole
-    requests in order, cycling over the batch, until about budget_s of CPU
-    time (at least one request), one BLAS thread."""
+def host_info() -> dict:
+    """The host's CPU model, core counts and the BLAS numpy runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(avail, share) if share > 0 else avail
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    if blas == "unknown":
+        try:
+            cfg = np.show_config(mode="dicts")
+            b = cfg["Build Dependencies"]["blas"]
+            blas = f"{b.get('name')} {b.get('version')}"
+        except Exception:
+            pass
+    return dict(cpu_model=model, nproc=os.cpu_count(), cpus_available=avail, threads=threads, blas=blas)
+
+
+def cpu_baseline(wd, runs: int = 3, prefill_requests=(0, 1, 2, 3)):
+    """The float64 oracle on the host's cores (BLAS threads = the CPU share
+    this process has: OMP_NUM_THREADS when set, else every available core),
+    median of `runs` runs of each sample: the whole batch-decode workload
+    (oracle GB/s over the same algorithmic bytes as the GPU figure) and
+    requests `prefill_requests` of the causal-prefill workload (oracle
+    GFLOP/s over their visible pairs)."""
     from threadpoolctl import threadpool_limits
 
     import oracle.attention as OA
+    from workloads import make_workload
 
-    done, t_used, nbytes = 0, 0.0, 0
-    B = len(w["kv_lens"])
-    per_tok = w["num_kv_heads"] * w["head_dim"] * ELEM[w["kv_dtype"]] * 2
-    with threadpool_limits(limits=1):
-        while done == 0 or t_used < budget_s:
-            i = done % B
+    info = host_info()
+    nb = decode_bytes(wd)
+    wp = make_workload("causal_prefill")
+    sub = list(prefill_requests)
+    qo, kv = wp["qo_lens"][sub], wp["kv_lens"][sub]
+    pflops = prefill_flops(dict(wp, qo_lens=qo, kv_lens=kv))
+    dt, pt = [], []
+    with threadpool_limits(limits=info["threads"]):
+        for _ in range(runs):
             t0 = time.perf_counter()
-            OA.batch_decode(w, requests=[i])
-            t_used += time.perf_counter() - t0
-            nbytes += int(w["kv_lens"][i]) * per_tok
-            done += 1
-    gbs = nbytes / t_used / 1e9
-    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{done} requests of the batch-decode workload taken in order, cycling over its {B} "
-                       f"({done / B:.1f} passes, {nbytes / 1e6:.1f} MB of fp8 K/V), {t_used:.1f} s, "
-                       f"float64 numpy, 1 thread")
+            OA.batch_decode(wd)
+            dt.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            OA.batch_prefill(wp, causal=True, requests=sub)
+            pt.append(time.perf_counter() - t0)
+    d_s, p_s = float(np.median(dt)), float(np.median(pt))
+    return dict(value=round(nb / d_s / 1e9, 4), unit="GB/s", cores=info["threads"], kind="oracle",
+                sample=f"the whole batch-decode workload ({len(wd['kv_lens'])} requests, {nb / 1e6:.1f} MB "
+                       f"algorithmic), float64 numpy, median of {runs} runs",
+                seconds=[round(x, 3) for x in dt], nproc=info["nproc"], cpus_available=info["cpus_available"],
+                cpu_model=info["cpu_model"], blas=info["blas"],
+                prefill={"value": round(pflops / p_s / 1e9, 3), "unit": "GFLOP/s",
+                         "sample": f"requests {sub} of the causal-prefill workload ({pflops / 1e9:.1f} GFLOP of "
+                                   f"visible pairs), median of {runs} runs",
+                         "seconds": [round(x, 3) for x in pt]})
 
 
 def main():
@@ -341,7 +401,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="identical K/V pool copies rotated across steps")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-runs", type=int, default=3, help="runs of each oracle sample (median reported)")
     ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all",
                     help="run one path only (for per-kernel counter passes)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -394,6 +454,9 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS_16, 4),
                          "traffic": measured_traffic("prefill", pw["name"]), "flops_per_launch": flops},
             "dtype": "f16",
+            "copies_rotated": 3,
+            "rotation": "3 full sets of q, K/V pools, o and lse (about 220 MB each) rotated across the steps, so no "
+                        "step finds the previous step's lines in the 256 MB last-level cache",
         }
         if not args.no_extra:
             _, _, r_ev = run_prefill_bench(args.prefill_steps, 3, ragged=True)
@@ -419,7 +482,12 @@ def main():
         copy_gbs = round(copy_bandwidth(), 1)
         print(f"# plain device copy: {copy_gbs} GB/s", file=sys.stderr, flush=True)
 
-    cpu = None if (args.no_cpu or args.only == "prefill") else cpu_baseline(w, args.cpu_budget)
+    cpu = None if (args.no_cpu or args.only == "prefill") else cpu_baseline(w, args.cpu_runs)
+    if cpu is not None and prefill is not None:
+        prefill["cpu_baseline"] = cpu["prefill"]
+    if cpu is not None:
+        print(f"# oracle on {cpu['cores']} threads ({cpu['cpu_model']}, {cpu['blas']}): decode {cpu['value']} GB/s, "
+              f"prefill {cpu['prefill']['value']} GFLOP/s", file=sys.stderr, flush=True)
 
     out = {
         "metric": METRIC,

@@ -296,7 +296,7 @@ fi_status fi_single_decode(const void* q, fi_dtype q_dtype, const void* k, const
  * attention kernels use (no scaling; the e4m3fnuz values, which the kernels
  * hold as value * 2^-7 with 2^7 folded into their scales, are returned as the
  * values themselves).  src in {E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ}, dst in
- * {F16, BF16}; the fnuz NaN code 0x80 reads as -0;
+ * {F16, BF16}; the fnuz NaN code 0x80 reads as a quiet NaN;
  * codes [dev] [n] bytes, out [dev] [n] 2-byte values.  This makes the
  * conversion testable code by code ([C] design notes: the vec_cast paragraph
  * records a decoder with the wrong bias and broken denormals that no test

@@ -27,7 +27,8 @@ What is computed, and where the pages state it:
       - sm_scale defaults to 1/sqrt(head_dim);
       - lse is the natural-log log-sum-exp of the scaled logits;
       - a row with no visible key has o = 0 and lse = -inf (the identity of the
-        state merge).
+        state merge); a NaN stored in K or V is not an empty row, it
+        propagates through the arithmetic as IEEE floats do.
   * The split-KV state merge (PR #2148, the fixed_split_size /
     disable_split_kv plan arguments): L = ln sum_c exp(lse_c),
     o = sum_c exp(lse_c - L) o_c.
@@ -125,8 +126,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool, sm_s
         s = s.reshape(n_q, group, n_kv)
         mask = np.broadcast_to(allowed[:, None, :], s.shape)
         s = np.where(mask, s, -np.inf)
-        m = s.max(axis=-1, keepdims=True)  # -inf on empty rows
-        has = np.isfinite(m)
+        m = s.max(axis=-1, keepdims=True)  # -inf on empty rows; NaN if a visible logit is NaN
+        # a row is empty when the mask leaves it no key; a NaN stored in K or V
+        # is not an empty row: it propagates through exp and the sums
+        has = np.broadcast_to(allowed.any(axis=-1)[:, None, None], m.shape)
         m_safe = np.where(has, m, 0.0)
         p = np.exp(s - m_safe)  # exp(-inf) = 0 on masked entries
         denom = p.sum(axis=-1, keepdims=True)
@@ -252,7 +255,7 @@ def merge_states(o_parts: np.ndarray, lse_parts: np.ndarray):
     lse_parts = np.asarray(lse_parts, dtype=np.float64)
     o_parts = np.asarray(o_parts, dtype=np.float64)
     m = lse_parts.max(axis=0)
-    has = np.isfinite(m)
+    has = ~np.all(np.isneginf(lse_parts), axis=0)  # a NaN state propagates
     m_safe = np.where(has, m, 0.0)
     wts = np.exp(lse_parts - m_safe)  # [C, ...]
     tot = wts.sum(axis=0)

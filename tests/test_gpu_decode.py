@@ -9,7 +9,8 @@ combinations decode admits (fnuz caches included), forced split-KV; and the inva
 bitwise determinism, bitwise page-permutation invariance, an fp8 run equal
 bitwise to a run on the same values pre-widened to q's type (the equivalence
 design of "fp8 KV cache in the in-tree prefill kernel", Test plan), the
-k_scale fold, constant V, NaN-poisoned padding and unreferenced pages, and a
+k_scale fold, constant V, NaN-poisoned padding and unreferenced pages (OCP and
+fnuz), a NaN code in the cache reaching exactly the rows that read it, a
 non-default (head-major) pool layout; batches past the planner's limits (900
 requests: prefix sums scanned on the device; 1100: fixed chunks) and a
 page-size-1 request spanning three page-id windows.
@@ -21,7 +22,7 @@ import torch
 import oracle.attention as OA
 from oracle.fp8 import fp8_table
 from attention_paged_fp8_amd import fi
-from workloads import make_paged, make_workload
+from workloads import NAN_BITS, make_paged, make_workload
 from gpu_util import (O_TOL, T2, assert_parity, dev_2byte, paged_kv, run_decode, say, upload, workspace_for)
 
 pytestmark = pytest.mark.gpu
@@ -38,10 +39,8 @@ def test_fp8_widen_all_codes_bitwise(gpu_device, src, dst):
     fi.fi_fp8_widen(codes, src, out)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
-    ref = fp8_table(src)[codes.cpu().numpy()].copy()
-    if src.endswith("fnuz"):
-        ref[codes.cpu().numpy() == 0x80] = -0.0  # the fnuz NaN code reads as -0 (documented)
-    nan = np.isnan(ref)
+    ref = fp8_table(src)[codes.cpu().numpy()]
+    nan = np.isnan(ref)  # OCP e4m3 0x7F/0xFF, e5m2 0x7D-0x7F/0xFD-0xFF, fnuz 0x80
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], ref[~nan])
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 stays -0
@@ -172,15 +171,14 @@ def test_dtype_decode_refusals_with_real_tensors(gpu_device):
 @pytest.mark.parametrize("kvd", ["e4m3fnuz", "e5m2fnuz"])
 def test_fnuz_batch_decode_shapes_and_single(gpu_device, kvd):
     """The batch-decode shapes (64 requests of 512..4096 tokens, 32/8 heads,
-    page 16 shuffled) over an fnuz cache, whole requests against the oracle;
+    page 16 shuffled) over an fnuz cache, every request against the oracle;
     and fi_single_decode over one request's rows."""
     say("fnuz batch_decode shapes", kvd)
     w = make_workload("batch_decode", kvd=kvd)
     d = upload(w, gpu_device)
     og, lg, _ = run_decode(w, d)
-    reqs = [0, 17, 40, 63]
-    o_ref, l_ref = OA.batch_decode(w, requests=reqs)
-    assert_parity(og[reqs], lg[reqs], o_ref[reqs], l_ref[reqs], "bf16", f"{kvd} batch decode")
+    o_ref, l_ref = OA.batch_decode(w)
+    assert_parity(og, lg, o_ref, l_ref, "bf16", f"{kvd} batch decode")
     i = 5
     pages = w["indices"][w["indptr"][i]:w["indptr"][i + 1]]
     n = int(w["kv_lens"][i])
@@ -332,7 +330,7 @@ def test_fnuz_outside_ocp_codes(gpu_device, kvd, q, plant):
         planted = (0x7F, 0xFF)
     else:
         outside = lambda pool: ((pool & 0x78) == 0) & ((pool & 0x7F) != 0)
-        repl = lambda pool, sel: pool[sel] & 0x80  # tiny -> +-0
+        repl = lambda pool, sel: 0  # tiny -> +0 (0x80 is the NaN code)
         planted = (0x01, 0x06, 0x85, 0x87)
     for pool in (kp, vp):
         sel = vsel & outside(pool)
@@ -397,15 +395,41 @@ def test_constant_v(gpu_device):
     np.testing.assert_allclose(o, exp.astype(np.float16).astype(np.float64), rtol=2e-3, atol=1e-6)
 
 
-def test_poisoned_pages_stay_finite(gpu_device):
-    """Unused slots and unreferenced pages hold NaN codes; outputs stay finite."""
-    say("poisoned pages")
-    w = _mid_workload(extra_pages=50)
-    assert np.isnan(fp8_table("e4m3")[w["k_pool"][~w["valid"]]]).all()
+@pytest.mark.parametrize("kvd", ["e4m3", "e4m3fnuz", "e5m2fnuz"])
+def test_poisoned_pages_stay_finite(gpu_device, kvd):
+    """Unused slots and unreferenced pages hold the format's NaN code (0x7F
+    OCP, 0x80 fnuz); outputs stay finite, so nothing outside the requests'
+    tokens is read."""
+    say("poisoned pages", kvd)
+    w = _mid_workload(kvd=kvd, extra_pages=50)
+    assert np.isnan(fp8_table(kvd)[w["k_pool"][~w["valid"]]]).all()
     d = upload(w, gpu_device)
     o, l, _ = run_decode(w, d, split="128")
     o_ref, l_ref = OA.batch_decode(w)
-    assert_parity(o, l, o_ref, l_ref, "bf16", "poisoned")
+    assert_parity(o, l, o_ref, l_ref, "bf16", f"poisoned {kvd}")
+
+
+@pytest.mark.parametrize("split", [None, "128"])
+@pytest.mark.parametrize("kvd", ["e4m3", "e4m3fnuz", "e5m2fnuz"])
+def test_nan_code_propagates(gpu_device, kvd, split):
+    """One K element of one request and kv head set to the format's NaN code
+    (0x7F for OCP e4m3, 0x80 for fnuz): the q heads of that kv head in that
+    request come out NaN, as in the oracle, and every other output matches it
+    -- a NaN in an fnuz cache propagates as one in an OCP cache does."""
+    say("NaN code propagates", kvd, split)
+    w = _mid_workload(kvd=kvd)
+    i, g = 2, 5
+    pg = w["indices"][w["indptr"][i] + 3]
+    w["k_pool"][pg, 7, g, 17] = NAN_BITS[kvd]
+    d = upload(w, gpu_device)
+    og, lg, _ = run_decode(w, d, split=split)
+    o_ref, l_ref = OA.batch_decode(w)
+    bad = np.zeros(og.shape[:2], dtype=bool)
+    bad[i, 4 * g:4 * g + 4] = True  # 32 q heads over 8 kv heads
+    assert np.isnan(o_ref[bad]).all() and np.isnan(l_ref[bad]).all()
+    assert np.isnan(og[bad]).all(), "the rows that read the NaN code are not NaN"
+    assert np.isnan(lg[bad]).all()
+    assert_parity(og[~bad], lg[~bad], o_ref[~bad], l_ref[~bad], "bf16", f"NaN code {kvd}, other rows")
 
 
 def test_head_major_pool_layout(gpu_device):

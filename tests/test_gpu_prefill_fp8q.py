@@ -87,22 +87,9 @@ def test_causal_prefill_fp8q_full_size(gpu_device):
     og, lg = run_fp8q(w, d)
     og2, lg2 = run_fp8q(w, d)
     assert np.array_equal(og, og2) and np.array_equal(lg, lg2), "fp8-query prefill is not deterministic"
-    reqs = [0, 9]
-    o_ref, l_ref = OA.batch_prefill(w, causal=True, requests=reqs)
-    qi = w["qo_indptr"]
-    for i in reqs:
-        a, b = int(qi[i]), int(qi[i + 1])
-        assert_parity(og[a:b], lg[a:b], o_ref[a:b], l_ref[a:b], "f16", f"causal-prefill workload fp8q request {i}")
-    rng = np.random.default_rng(1)
-    toks, heads = [], []
-    for i in range(len(w["qo_lens"])):
-        a, b = int(qi[i]), int(qi[i + 1])
-        for t in {a, b - 1, int(rng.integers(a, b))}:
-            for h in rng.choice(32, 3, replace=False):
-                toks.append(t)
-                heads.append(int(h))
-    o_s, l_s = OA.attention_rows(w, toks, heads, causal=True)
-    assert_parity(og[toks, heads], lg[toks, heads], o_s, l_s, "f16", "causal-prefill workload fp8q sampled rows")
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    err = assert_parity(og, lg, o_ref, l_ref, "f16", "causal-prefill workload, fp8 query")
+    print(f"causal-prefill workload, fp8 query: max |o - oracle| = {err:.3e}")
 
 
 @pytest.mark.parametrize("causal", [True, False])

@@ -17,7 +17,9 @@ Pins, and what fixes them independently of the oracle's own code:
     (the fold recorded in "fp8 KV cache in the in-tree prefill kernel",
     Test plan, k_scale/v_scale item); the same for q_scale of an fp8 query;
   * causal: with no prefix, query row 0 sees only key 0 and the last row sees
-    every key.
+    every key;
+  * a NaN stored in K poisons exactly the rows that read it (brute force), and
+    the contiguous single-decode form equals the scalar loops.
 """
 import importlib.util
 import math
@@ -34,7 +36,8 @@ from workloads import make_paged
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-_TDT = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+_TDT = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
+        "e4m3fnuz": torch.float8_e4m3fnuz, "e5m2fnuz": torch.float8_e5m2fnuz}
 
 
 def _torch_decode(raw, dtype):
@@ -70,19 +73,20 @@ def brute_force(w, causal, sm_scale=None):
         for r in range(n_q):
             for h in range(hq):
                 g = h // grp
-                ws, acc = 0.0, np.zeros(d)
+                ws, acc, seen = 0.0, np.zeros(d), 0
                 for t in range(n_kv):
                     if causal and t > r + n_kv - n_q:
                         continue
+                    seen += 1
                     s = 0.0
                     for c in range(d):
                         s += q[a + r, h, c] * keys[t][g, c]
                     e = math.exp(s * scale)
                     ws += e
                     acc = acc + e * vals[t][g]
-                if ws > 0:
+                if seen > 0:  # a NaN logit makes ws NaN, and o and lse with it
                     o[a + r, h] = acc / ws
-                    lse[a + r, h] = math.log(ws)
+                    lse[a + r, h] = math.log(ws) if ws == ws else math.nan
     return o, lse
 
 
@@ -268,7 +272,45 @@ def pin_empty_request(M):
     np.testing.assert_allclose(l[[0, 2]], lb[[0, 2]], atol=1e-12)
 
 
-PINS = [pin_empty_request, pin_brute_force_decode, pin_brute_force_prefill, pin_closed_forms, pin_weights_sum_to_one,
+def pin_nan_propagates(M):
+    """A NaN code in one K element of one request and kv head: the q heads of
+    that kv head in that request come out NaN (brute force: exp(NaN) poisons
+    the sums), every other output is unchanged; an empty row stays o = 0,
+    lse = -inf."""
+    w = _tiny_decode(11, kvd="e4m3", lens=(5, 9, 3))
+    i, g = 1, 1
+    pg = w["indices"][w["indptr"][i]]
+    w["k_pool"][pg, 2, g, 3] = 0x7F  # OCP e4m3 NaN
+    o, l = M.batch_decode(w)
+    ob, lb = brute_force(w, causal=False)
+    bad = np.zeros(o.shape[:2], dtype=bool)
+    bad[i, 2 * g:2 * g + 2] = True  # 4 q heads over 2 kv heads
+    assert np.isnan(ob[bad]).all() and np.isnan(lb[bad]).all()
+    assert np.isnan(o[bad]).all() and np.isnan(l[bad]).all()
+    np.testing.assert_allclose(o[~bad], ob[~bad], atol=1e-12)
+    np.testing.assert_allclose(l[~bad], lb[~bad], atol=1e-12)
+    # merge: a NaN partial state poisons the merged one, an empty one does not
+    om, lm = M.merge_states(np.array([[[1.0, 2.0]], [[3.0, 4.0]]]), np.array([[np.nan], [0.5]]))
+    assert np.isnan(om).all() and np.isnan(lm).all()
+    om, lm = M.merge_states(np.array([[[1.0, 2.0]], [[3.0, 4.0]]]), np.array([[-np.inf], [0.5]]))
+    np.testing.assert_allclose(om[0], [3.0, 4.0], atol=1e-15)
+
+
+def pin_single_decode(M):
+    """single_decode on contiguous K/V rows against the scalar-loop definition
+    of a one-request paged workload holding the same rows (pages contiguous)."""
+    for seed, kvd, q in ((12, "e4m3", "f16"), (13, "e5m2fnuz", "bf16"), (14, "bf16", "f16")):
+        w = make_paged(seed, kv_lens=[11], hq=4, hkv=2, d=8, page=4, q=q, kvd=kvd, contiguous=True)
+        n = int(w["kv_lens"][0])
+        k = w["k_pool"].reshape(-1, 2, 8)[:n]
+        v = w["v_pool"].reshape(-1, 2, 8)[:n]
+        o, l = M.single_decode(w["q"][0], q, k, v, kvd, w["k_scale"], w["v_scale"])
+        ob, lb = brute_force(w, causal=False)
+        np.testing.assert_allclose(o, ob[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb[0], rtol=0, atol=1e-12)
+
+
+PINS = [pin_empty_request, pin_nan_propagates, pin_single_decode, pin_brute_force_decode, pin_brute_force_prefill, pin_closed_forms, pin_weights_sum_to_one,
         pin_page_permutation, pin_decode_equals_prefill_one_query, pin_split_merge,
         pin_gqa_equals_repeated_mha, pin_kscale_fold, pin_fp8_query, pin_causal_rows, pin_sampled_rows]
 
@@ -293,6 +335,8 @@ MUTATIONS = {
     "merge_unweighted": ("o = (coef[..., None] * o_parts).sum(axis=0)", "o = o_parts.mean(axis=0)"),
     "transposed_pv": ("og = (w.reshape(n_q * group, n_kv) @ vg)", "og = (w.reshape(n_q * group, n_kv) @ vg[::-1])"),
     "default_scale_wrong": ("return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    "nan_as_empty_row": ("has = np.broadcast_to(allowed.any(axis=-1)[:, None, None], m.shape)", "has = np.isfinite(m)"),
+    "single_v_scale_dropped": ("v = decode_elements(v_raw, kv_dtype) * float(v_scale)", "v = decode_elements(v_raw, kv_dtype)"),
     "q_scale_dropped": ('return decode_elements(w["q"], w["q_dtype"]) * float(w.get("q_scale", 1.0))',
                         'return decode_elements(w["q"], w["q_dtype"])'),
 }
