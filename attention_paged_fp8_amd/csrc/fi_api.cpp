@@ -222,10 +222,16 @@ size_t partial_bytes(int64_t batch, int64_t max_chunks, int64_t hqo, int64_t d) 
   return (size_t)(batch * max_chunks * hqo * (d + 1) * 4);
 }
 
+// use_scratch: the allocation-free call -- the split-KV state goes to the
+// library's own per-device scratch array (at most fi::kDecodeScratchBytes)
+// instead of a caller's workspace; `workspace` is then NULL and its address
+// is looked up only once every check has passed.
 fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_dtype kv_dtype, fi_dtype o_dtype,
                      int32_t batch, int32_t head_dim, const int32_t* indptr_h, const int32_t* last_page_len_h,
                      int32_t page_size, int64_t max_kv, int64_t total_kv, void* workspace, size_t workspace_bytes,
-                     float sm_scale, float k_scale, float v_scale, hipStream_t stream) {
+                     float sm_scale, float k_scale, float v_scale, hipStream_t stream, bool use_scratch = false) {
+  const bool have_ws = workspace != nullptr || use_scratch;
+  if (use_scratch) workspace_bytes = fi::kDecodeScratchBytes;
   // Workgroup shape: up to 4 waves, one per (kv head, 16-row slice of its GQA
   // group); the heads of a workgroup are adjacent, so each token's rows of
   // those heads are read as one contiguous run.
@@ -256,7 +262,7 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   // Balanced split: equal slices of the (group, request, token) space, one per
   // workgroup slot of the device (the default whenever a workspace is given).
   p.balanced = 0;
-  if (workspace && !forced && batch <= fi::kBalancedMaxBatch && total_kv > 0) {
+  if (have_ws && !forced && batch <= fi::kBalancedMaxBatch && total_kv > 0) {
     // Workgroups: the device's resident capacity (CUs x occupancy), except
     // that short streams run better at 2 per CU -- fewer, longer slices split
     // fewer requests and spread start-up over more bytes (measured: a slice
@@ -313,7 +319,7 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
     }
   }
   if (!p.balanced) {
-    const int64_t chunk = plan_chunk(max_kv, total_kv, groups, workspace != nullptr);
+    const int64_t chunk = plan_chunk(max_kv, total_kv, groups, have_ws);
     const int64_t max_chunks = std::max<int64_t>(1, ceil_div(max_kv, chunk));
     if (max_chunks * groups * (int64_t)batch > 0x7fffffff)
       return fail(FI_E_SHAPE, fn, "the split needs more than 2^31 workgroups");
@@ -322,10 +328,18 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
     merge = max_chunks > 1;
   }
   const size_t need = merge ? partial_bytes(batch, p.max_chunks, p.num_qo_heads, head_dim) + (size_t)batch * groups * 4 : 0;
+  if (need > 0 && use_scratch && need > workspace_bytes)
+    return fail(FI_E_WORKSPACE, fn, "this batch's split-KV state needs %zu bytes; the allocation-free call holds at "
+                "most %zu bytes of scratch (FI_DECODE_SCRATCH_BYTES): call fi_batch_decode_paged with a workspace "
+                "of fi_decode_workspace_bytes() instead", need, workspace_bytes);
   if (need > 0 && workspace_bytes < need)
     return fail(FI_E_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the %zu bytes this split needs "
                 "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
-  if (need > 0 && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
+  if (need > 0 && !use_scratch && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
+  if (need > 0 && use_scratch && batch > 0) {
+    hipError_t e = fi::decode_scratch(&workspace);
+    if (e != hipSuccess) return fail(FI_E_HIP, fn, "scratch address lookup failed: %s", hipGetErrorString(e));
+  }
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
   // e4m3fnuz codes are widened to value * 2^-7 (exactly); the 2^7 joins the scales
   if (kv_dtype == FI_F8_E4M3_FNUZ) {
@@ -481,7 +495,8 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
 // Batched paged decode after the dtype checks (q_scale: 1 for a 2-byte query).
 static fi_status decode_paged(const char* fn, const void* q, fi_dtype q_dtype, float q_scale, int32_t batch,
                               int32_t num_qo_heads, const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse,
-                              float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                              float sm_scale, void* workspace, size_t workspace_bytes, void* stream,
+                              bool use_scratch = false) {
   fi_status st;
   if (batch < 0) return fail(FI_E_SHAPE, fn, "batch=%d is outside [0, 2^31)", batch);
   if ((st = check_heads(fn, num_qo_heads, kv->num_kv_heads, kv->head_dim)) != FI_OK) return st;
@@ -514,7 +529,7 @@ static fi_status decode_paged(const char* fn, const void* q, fi_dtype q_dtype, f
   // q_scale joins k_scale in the logit scale (both multiply the fp32 products)
   return run_decode(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, kv->head_dim, kv->indptr_h, kv->last_page_len_h,
                     kv->page_size, max_kv, total_kv, workspace, workspace_bytes, sm_scale, kv->k_scale * q_scale,
-                    kv->v_scale, reinterpret_cast<hipStream_t>(stream));
+                    kv->v_scale, reinterpret_cast<hipStream_t>(stream), use_scratch);
 }
 
 fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
@@ -526,6 +541,17 @@ fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, 
   if (st != FI_OK) return st;
   return decode_paged(fn, q, q_dtype, 1.0f, batch, num_qo_heads, kv, o, o_dtype, lse, sm_scale, workspace,
                       workspace_bytes, stream);
+}
+
+fi_status fi_batch_decode_paged_noalloc(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
+                                        const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
+                                        void* stream) {
+  static const char* fn = "fi_batch_decode_paged_noalloc";
+  if (!kv) return fail(FI_E_ARG, fn, "kv must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv->k_dtype, kv->v_dtype, false);
+  if (st != FI_OK) return st;
+  return decode_paged(fn, q, q_dtype, 1.0f, batch, num_qo_heads, kv, o, o_dtype, lse, sm_scale, nullptr, 0, stream,
+                      true);
 }
 
 fi_status fi_batch_decode_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, int32_t batch,

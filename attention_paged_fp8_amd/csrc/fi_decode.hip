@@ -38,6 +38,7 @@
 // single rounding) or, when the request is split into several chunks, an fp32
 // partial (output, log-sum-exp) that merge_kernel combines.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fi_device.hpp"
@@ -611,6 +612,38 @@ __global__ __launch_bounds__(256) void widen_kernel(const uint8_t* codes, int64_
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     if (i + j < n) out[i + j] = v[j];
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode call (fi_batch_decode_paged_noalloc):
+// the split-KV partial states and piece counts live in this array instead of
+// a caller's workspace.  Every GPU holds its own copy until the process ends.
+// Host code never names the array itself (on the host the name is only a
+// stand-in, not a device address): it asks the runtime for the current
+// device's address once per device and passes that pointer to the kernels as
+// the workspace.  Nothing in it needs to start at zero: a call writes every
+// piece count and every partial state it later reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

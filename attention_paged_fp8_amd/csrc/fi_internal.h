@@ -124,4 +124,11 @@ hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_f
                           bool ragged, hipStream_t s);
 hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int dst_fmt, void* out, hipStream_t s);
 
+// Split-KV scratch of the allocation-free decode call: a file-scope device
+// array of kDecodeScratchBytes in the decode translation unit, one copy per
+// GPU.  decode_scratch() returns the current device's address of it (looked
+// up once per device with hipGetSymbolAddress and cached).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fi

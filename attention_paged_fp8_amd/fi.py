@@ -37,7 +37,8 @@ STATUS = {0: "FI_OK", 1: "FI_E_DTYPE", 2: "FI_E_SHAPE", 3: "FI_E_ARG", 4: "FI_E_
 EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_decode_paged_fp8q",
            "fi_batch_prefill_paged", "fi_batch_prefill_paged_fp8q", "fi_batch_prefill_ragged",
            "fi_batch_prefill_ragged_fp8q", "fi_single_prefill", "fi_single_prefill_fp8q", "fi_single_decode",
-           "fi_fp8_widen")
+           "fi_fp8_widen", "fi_batch_decode_paged_noalloc")
+DECODE_SCRATCH_BYTES = 32 << 20  # FI_DECODE_SCRATCH_BYTES
 
 
 class FiError(Exception):
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.fi_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.fi_batch_decode_paged.restype = en
     L.fi_batch_decode_paged.argtypes = [vp, en, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz, vp]
+    L.fi_batch_decode_paged_noalloc.restype = en
+    L.fi_batch_decode_paged_noalloc.argtypes = [vp, en, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp]
     L.fi_batch_decode_paged_fp8q.restype = en
     L.fi_batch_decode_paged_fp8q.argtypes = [vp, en, f32, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz,
                                              vp]
@@ -208,6 +211,19 @@ def fi_batch_decode_paged(q, kv: PagedKV, o, *, q_dtype=None, o_dtype=None, lse=
         int(batch if batch is not None else q.shape[0]), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
         ctypes.byref(kv), _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale),
         _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+    check(st)
+    return o
+
+
+def fi_batch_decode_paged_noalloc(q, kv: PagedKV, o, *, q_dtype=None, o_dtype=None, lse=None, sm_scale=0.0,
+                                  batch=None, num_qo_heads=None, stream=None):
+    """fi_batch_decode_paged with the split-KV state in the library's own
+    per-device scratch (no workspace argument, nothing allocated)."""
+    st = lib().fi_batch_decode_paged_noalloc(
+        _ptr(q), _dt(q_dtype if q_dtype is not None else q.dtype),
+        int(batch if batch is not None else q.shape[0]), int(num_qo_heads if num_qo_heads is not None else q.shape[1]),
+        ctypes.byref(kv), _ptr(o), _dt(o_dtype if o_dtype is not None else o.dtype), _ptr(lse), float(sm_scale),
+        _stream(stream, q, o))
     check(st)
     return o
 

@@ -165,6 +165,24 @@ fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, 
                                 const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Batched decode that allocates nothing and takes no workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Arguments, dtype rules,
+ * results and the split-KV plan are those of fi_batch_decode_paged with a
+ * workspace, and the output is bit-identical to it; the split-KV partial
+ * states go to a scratch array the library holds in device memory, one copy
+ * per GPU, FI_DECODE_SCRATCH_BYTES long, kept until the process ends.
+ * A batch whose split needs more scratch than that is refused with
+ * FI_E_WORKSPACE (no kernel launched; fi_batch_decode_paged with a workspace
+ * of fi_decode_workspace_bytes() has no such limit).  No memory is allocated,
+ * set or copied.  Every call on a GPU shares that GPU's scratch, so two calls
+ * that overlap in time on one GPU (different streams, or host threads) race:
+ * the caller serialises them, e.g. on one stream. */
+#define FI_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+fi_status fi_batch_decode_paged_noalloc(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
+                                        const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
+                                        void* stream);
+
 /* Batched decode with an fp8 query ([A]: fp8 attention in decode.py; review
  * comments: q_scale folded into sm_scale for the first product).
  *   q        [dev] [batch, num_qo_heads, head_dim] fp8 codes, q_dtype in

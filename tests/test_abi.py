@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -429,6 +429,29 @@ def test_workspace_too_small(L, monkeypatch):
     kv, keep = _kv(ptrs=True, lens=(1000, 300))
     st = _decode(L, kv, qp=0x10000, op=0x10000, ws=0x10000, wsb=16)
     assert st == 4 and "workspace_bytes=16" in _err(L), _err(L)
+
+
+def test_scratch_size_matches_header():
+    m = re.search(r"#define FI_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fi.DECODE_SCRATCH_BYTES
+
+
+@no_gpu
+def test_noalloc_refuses_a_split_beyond_its_scratch(L, monkeypatch):
+    """A split whose partial states exceed the allocation-free call's scratch
+    is refused with FI_E_WORKSPACE before any HIP call; the dtype refusals come
+    first, as in fi_batch_decode_paged."""
+    monkeypatch.setenv("FI_SPLIT_KV", "64")
+    kv, keep = _kv(ptrs=True, hkv=8, d=128, lens=(70000, 10))  # 1094 pieces x 64 heads x 129 floats x 2
+    fake = 0x10000
+    st = L.fi_batch_decode_paged_noalloc(fake, fi.DTYPES["f16"], 2, 64, ctypes.byref(kv), fake, 0, None, 0.0, None)
+    assert st == 4 and "allocation-free call holds at most 33554432 bytes" in _err(L), _err(L)
+    kv2, keep2 = _kv("e4m3", "e5m2", ptrs=True)
+    st = L.fi_batch_decode_paged_noalloc(fake, fi.DTYPES["f16"], 2, 4, ctypes.byref(kv2), fake, 0, None, 0.0, None)
+    assert st == 1 and "fi_batch_decode_paged_noalloc: k has dtype float8_e4m3fn but v has dtype float8_e5m2" in _err(L)
+    st = L.fi_batch_decode_paged_noalloc(fake, fi.DTYPES["f16"], 2, 4, ctypes.byref(kv2), fake, fi.DTYPES["e4m3"],
+                                         None, 0.0, None)
+    assert st == 1 and "an fp8 output is not supported" in _err(L)
 
 
 @no_gpu
