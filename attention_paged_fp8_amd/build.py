@@ -1,6 +1,13 @@
 """Build libfi.so (the HIP library behind include/fi.h) in-tree for gfx950.
 
-    python -m attention_paged_fp8_amd.build        # or build() from Python
+    python -m attention_paged_fp8_amd.build             # or build() from Python
+    python -m attention_paged_fp8_amd.build --sanitize  # host front end under ASan + UBSan
+
+--sanitize builds a second library, attention_paged_fp8_amd/_sanitize/libfi.so,
+whose host front end (fi_api.cpp: argument checks, planning, launches) is
+compiled and linked with AddressSanitizer and UndefinedBehaviorSanitizer
+(host code only; the kernels are built as usual).  sanitize_check.py runs the
+CPU tests of the C ABI against it.
 
 Every translation unit is compiled by hipcc for --offload-arch=gfx950 in
 parallel into _build/, then linked into attention_paged_fp8_amd/libfi.so.
@@ -23,8 +30,8 @@ LIB = os.path.join(HERE, "libfi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fi_api.cpp", "fi_decode.hip", "fi_prefill.hip"]
-HEADERS = ["fi_internal.h", "fi_device.hpp"]
+SOURCES = ["fi_api.cpp", "fi_decode.hip", "fi_prefill.hip", "fi_pod.hip"]
+HEADERS = ["fi_internal.h", "fi_device.hpp", "fi_decode_body.hpp", "fi_prefill_body.hpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
@@ -35,7 +42,11 @@ COMMON = [
 # element before it reaches arithmetic, so it produces no NaN; without IEEE-mode
 # NaN quieting its max reductions take one instruction per element instead of
 # three.  (The decode kernel gains nothing from this and spills with it.)
-PER_SOURCE = {"fi_prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# Host-only sanitizer flags of the --sanitize build (applied to fi_api.cpp and the link).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_LIB = os.path.join(HERE, "_sanitize", "libfi.so")
+PER_SOURCE = {"fi_prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+              "fi_pod.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str, extra: list[str], csrc: str = CSRC, build_dir: str = BUILD) -> str:
@@ -47,17 +58,23 @@ def _compile(src: str, extra: list[str], csrc: str = CSRC, build_dir: str = BUIL
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB, csrc: str = CSRC) -> str:
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB, csrc: str = CSRC,
+          sanitize: bool = False) -> str:
     """Compile every source and link the library (default libfi.so in the
-    package; `out`, `csrc` and `extra` build a variant elsewhere); returns its path."""
+    package; `out`, `csrc` and `extra` build a variant elsewhere; `sanitize`
+    builds the ASan + UBSan host front end into _sanitize/libfi.so); returns
+    its path."""
+    if sanitize and out == LIB:
+        out = SANITIZE_LIB
     build_dir = BUILD if out == LIB else os.path.splitext(out)[0] + "_build"
     os.makedirs(build_dir, exist_ok=True)
     extra = list(extra or [])
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    per = (lambda src: extra + SANITIZE) if sanitize else (lambda src: extra)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, csrc, build_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, per(s) if s == "fi_api.cpp" else extra, csrc, build_dir), SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *(SANITIZE if sanitize else []), *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -68,4 +85,6 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    args = sys.argv[1:]
+    san = "--sanitize" in args
+    build(verbose=True, extra=[a for a in args if a != "--sanitize"], sanitize=san)

@@ -222,25 +222,29 @@ size_t partial_bytes(int64_t batch, int64_t max_chunks, int64_t hqo, int64_t d) 
   return (size_t)(batch * max_chunks * hqo * (d + 1) * 4);
 }
 
-// use_scratch: the allocation-free call -- the split-KV state goes to the
-// library's own per-device scratch array (at most fi::kDecodeScratchBytes)
-// instead of a caller's workspace; `workspace` is then NULL and its address
-// is looked up only once every check has passed.
-fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_dtype kv_dtype, fi_dtype o_dtype,
-                     int32_t batch, int32_t head_dim, const int32_t* indptr_h, const int32_t* last_page_len_h,
-                     int32_t page_size, int64_t max_kv, int64_t total_kv, void* workspace, size_t workspace_bytes,
-                     float sm_scale, float k_scale, float v_scale, hipStream_t stream, bool use_scratch = false) {
-  const bool have_ws = workspace != nullptr || use_scratch;
-  if (use_scratch) workspace_bytes = fi::kDecodeScratchBytes;
-  // Workgroup shape: up to 4 waves, one per (kv head, 16-row slice of its GQA
+// The split-KV plan of a decode batch, for NW-wave workgroups: workgroup
+// shape (kv heads and GQA row slices per workgroup), then either the balanced
+// split (equal slices of the (group, request, token) space, one per
+// workgroup slot; needs a workspace) or fixed chunks.  `slots` > 0 gives the
+// number of balanced slices to aim for; 0 takes the device's resident
+// capacity for the 4-wave decode kernel with the rule below.  On return
+// *merge says whether some segment was split (or a request is empty) and
+// *need is the workspace the partial states take.
+template <class DP>
+fi_status plan_decode(const char* fn, DP& p, int nw, int slots, fi_dtype q_dtype, fi_dtype kv_dtype,
+                      fi_dtype o_dtype, int32_t batch, int32_t head_dim, const int32_t* indptr_h,
+                      const int32_t* last_page_len_h, int32_t page_size, int64_t max_kv, int64_t total_kv,
+                      bool have_ws, bool* merge_out, size_t* need_out) {
+  // Workgroup shape: up to nw waves, one per (kv head, 16-row slice of its GQA
   // group); the heads of a workgroup are adjacent, so each token's rows of
   // those heads are read as one contiguous run.
   const int nsub = (p.group + fi::kDecodeRows - 1) / fi::kDecodeRows;
   p.nsub = nsub;
-  p.spw = nsub <= fi::kDecodeWaves ? nsub : fi::kDecodeWaves;
-  const int max_hpw = fi::kDecodeWaves / p.spw;  // 4, 2 or 1
+  p.spw = nsub <= nw ? nsub : nw;
+  const int max_hpw = nw / p.spw;
+  const int max_shift = ilog2(nw);
   int hpw_shift = 0;
-  while (hpw_shift < 2 && (2 << hpw_shift) <= max_hpw && p.num_kv_heads % (2 << hpw_shift) == 0) ++hpw_shift;
+  while (hpw_shift < max_shift && (2 << hpw_shift) <= max_hpw && p.num_kv_heads % (2 << hpw_shift) == 0) ++hpw_shift;
   p.hpw_shift = hpw_shift;
   p.n_hgroups = p.num_kv_heads >> hpw_shift;
   p.n_sgroups = (nsub + p.spw - 1) / p.spw;
@@ -263,15 +267,17 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   // workgroup slot of the device (the default whenever a workspace is given).
   p.balanced = 0;
   if (have_ws && !forced && batch <= fi::kBalancedMaxBatch && total_kv > 0) {
-    // Workgroups: the device's resident capacity (CUs x occupancy), except
-    // that short streams run better at 2 per CU -- fewer, longer slices split
-    // fewer requests and spread start-up over more bytes (measured: a slice
-    // under ~640 KB of K/V loses at 3 per CU, one over ~850 KB gains).
-    int slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
-    const int cus = fi::device_cus();
-    if (slots > 0 && cus > 0 && slots / cus > 2) {
-      const int64_t row_bytes = (int64_t)(1 << hpw_shift) * head_dim * elem_bytes(kv_dtype) * 2;  // K + V per item
-      if (ceil_div(total_kv * groups, slots) * row_bytes < (640 << 10)) slots = 2 * cus;
+    if (slots <= 0) {
+      // Workgroups: the device's resident capacity (CUs x occupancy), except
+      // that short streams run better at 2 per CU -- fewer, longer slices split
+      // fewer requests and spread start-up over more bytes (measured: a slice
+      // under ~640 KB of K/V loses at 3 per CU, one over ~850 KB gains).
+      slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
+      const int cus = fi::device_cus();
+      if (slots > 0 && cus > 0 && slots / cus > 2) {
+        const int64_t row_bytes = (int64_t)(1 << hpw_shift) * head_dim * elem_bytes(kv_dtype) * 2;  // K + V per item
+        if (ceil_div(total_kv * groups, slots) * row_bytes < (640 << 10)) slots = 2 * cus;
+      }
     }
     if (slots > 0) {
       const int64_t W = total_kv * groups;
@@ -280,7 +286,7 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
       p.balanced = 1;
       p.slice = slice;
       p.pre_n = 0;
-      if (batch <= fi::kDecodePrefixMax && total_kv < 0x7fffffff) {
+      if (batch <= DP::kPrefixMax && total_kv < 0x7fffffff) {
         int64_t run = 0;
         for (int32_t i = 0; i < batch; ++i) {
           p.pre[i] = (int32_t)run;
@@ -327,19 +333,22 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
     p.max_chunks = (int32_t)max_chunks;
     merge = max_chunks > 1;
   }
-  const size_t need = merge ? partial_bytes(batch, p.max_chunks, p.num_qo_heads, head_dim) + (size_t)batch * groups * 4 : 0;
-  if (need > 0 && use_scratch && need > workspace_bytes)
-    return fail(FI_E_WORKSPACE, fn, "this batch's split-KV state needs %zu bytes; the allocation-free call holds at "
-                "most %zu bytes of scratch (FI_DECODE_SCRATCH_BYTES): call fi_batch_decode_paged with a workspace "
-                "of fi_decode_workspace_bytes() instead", need, workspace_bytes);
-  if (need > 0 && workspace_bytes < need)
-    return fail(FI_E_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the %zu bytes this split needs "
-                "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
-  if (need > 0 && !use_scratch && !aligned16(workspace)) return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
-  if (need > 0 && use_scratch && batch > 0) {
-    hipError_t e = fi::decode_scratch(&workspace);
-    if (e != hipSuccess) return fail(FI_E_HIP, fn, "scratch address lookup failed: %s", hipGetErrorString(e));
-  }
+  *merge_out = merge;
+  *need_out = merge ? partial_bytes(batch, p.max_chunks, p.num_qo_heads, head_dim) + (size_t)batch * groups * 4 : 0;
+  return FI_OK;
+}
+
+// Decode workgroups of a plan (the grid of the decode kernel or the decode
+// part of a fused launch).
+template <class DP>
+int64_t decode_workgroups(const DP& p, int32_t batch) {
+  return p.balanced ? (int64_t)p.n_wg : (int64_t)p.max_chunks * p.n_hgroups * p.n_sgroups * batch;
+}
+
+// Scales and the partial-state pointers of a planned decode.
+template <class DP>
+void finish_decode(DP& p, fi_dtype kv_dtype, int32_t batch, int32_t head_dim, float sm_scale, float k_scale,
+                   float v_scale, void* workspace, size_t need) {
   const float scale = (sm_scale > 0.f) ? sm_scale : 1.0f / std::sqrt((float)head_dim);
   // e4m3fnuz codes are widened to value * 2^-7 (exactly); the 2^7 joins the scales
   if (kv_dtype == FI_F8_E4M3_FNUZ) {
@@ -353,26 +362,72 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   p.part_o = need ? ws : nullptr;
   p.part_lse = need ? ws + npart * head_dim : nullptr;
   p.nch = need ? reinterpret_cast<int32_t*>(ws + npart * (head_dim + 1)) : nullptr;
+}
+
+// The split-KV merge of a planned decode (after its decode workgroups ran).
+template <class DP>
+hipError_t launch_decode_merge(const DP& p, fi_dtype o_dtype, int32_t batch, int32_t head_dim, hipStream_t stream) {
+  fi::MergeParams mp{};
+  mp.o = p.o;
+  mp.lse = p.lse;
+  mp.part_o = p.part_o;
+  mp.part_lse = p.part_lse;
+  mp.nch = p.nch;
+  mp.batch = batch;
+  mp.num_qo_heads = p.num_qo_heads;
+  mp.group = p.group;
+  mp.hpw_shift = p.hpw_shift;
+  mp.spw = p.spw;
+  mp.n_hgroups = p.n_hgroups;
+  mp.n_sgroups = p.n_sgroups;
+  mp.max_chunks = p.max_chunks;
+  mp.v_scale = p.v_scale;
+  return fi::launch_merge(mp, o_dtype, head_dim, batch, stream);
+}
+
+// Workspace checks of a planned decode; for the allocation-free call
+// (use_scratch) the scratch array's address is looked up here, after every
+// check has passed.
+fi_status decode_workspace(const char* fn, size_t need, void** workspace, size_t workspace_bytes, bool use_scratch,
+                           int32_t batch) {
+  if (need > 0 && use_scratch && need > workspace_bytes)
+    return fail(FI_E_WORKSPACE, fn, "this batch's split-KV state needs %zu bytes; the allocation-free call holds at "
+                "most %zu bytes of scratch (FI_DECODE_SCRATCH_BYTES): call fi_batch_decode_paged with a workspace "
+                "of fi_decode_workspace_bytes() instead", need, workspace_bytes);
+  if (need > 0 && workspace_bytes < need)
+    return fail(FI_E_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the %zu bytes this split needs "
+                "(fi_decode_workspace_bytes gives the bound)", workspace_bytes, need);
+  if (need > 0 && !use_scratch && !aligned16(*workspace))
+    return fail(FI_E_ARG, fn, "workspace must be 16-byte aligned");
+  if (need > 0 && use_scratch && batch > 0) {
+    hipError_t e = fi::decode_scratch(workspace);
+    if (e != hipSuccess) return fail(FI_E_HIP, fn, "scratch address lookup failed: %s", hipGetErrorString(e));
+  }
+  return FI_OK;
+}
+
+// use_scratch: the allocation-free call -- the split-KV state goes to the
+// library's own per-device scratch array (at most fi::kDecodeScratchBytes)
+// instead of a caller's workspace; `workspace` is then NULL and its address
+// is looked up only once every check has passed.
+fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_dtype kv_dtype, fi_dtype o_dtype,
+                     int32_t batch, int32_t head_dim, const int32_t* indptr_h, const int32_t* last_page_len_h,
+                     int32_t page_size, int64_t max_kv, int64_t total_kv, void* workspace, size_t workspace_bytes,
+                     float sm_scale, float k_scale, float v_scale, hipStream_t stream, bool use_scratch = false) {
+  const bool have_ws = workspace != nullptr || use_scratch;
+  if (use_scratch) workspace_bytes = fi::kDecodeScratchBytes;
+  bool merge = false;
+  size_t need = 0;
+  fi_status st = plan_decode(fn, p, fi::kDecodeWaves, 0, q_dtype, kv_dtype, o_dtype, batch, head_dim, indptr_h,
+                             last_page_len_h, page_size, max_kv, total_kv, have_ws, &merge, &need);
+  if (st != FI_OK) return st;
+  if ((st = decode_workspace(fn, need, &workspace, workspace_bytes, use_scratch, batch)) != FI_OK) return st;
+  finish_decode(p, kv_dtype, batch, head_dim, sm_scale, k_scale, v_scale, workspace, need);
   if (batch == 0) return FI_OK;
   hipError_t err = fi::launch_decode(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, stream);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(err));
   if (merge) {
-    fi::MergeParams mp{};
-    mp.o = p.o;
-    mp.lse = p.lse;
-    mp.part_o = p.part_o;
-    mp.part_lse = p.part_lse;
-    mp.nch = p.nch;
-    mp.batch = batch;
-    mp.num_qo_heads = p.num_qo_heads;
-    mp.group = p.group;
-    mp.hpw_shift = p.hpw_shift;
-    mp.spw = p.spw;
-    mp.n_hgroups = p.n_hgroups;
-    mp.n_sgroups = p.n_sgroups;
-    mp.max_chunks = p.max_chunks;
-    mp.v_scale = v_scale;
-    err = fi::launch_merge(mp, o_dtype, head_dim, batch, stream);
+    err = launch_decode_merge(p, o_dtype, batch, head_dim, stream);
     if (err != hipSuccess) return fail(FI_E_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(err));
   }
   return FI_OK;
@@ -383,13 +438,13 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
 // hardware's in-order dispatch approximates longest-processing-time
 // scheduling and no workgroup is launched for an empty query block.  Left
 // empty (grid order) when the pairs do not fit in the kernel arguments.
-void plan_prefill_order(fi::PrefillParams& p, int32_t batch, const int32_t* qo_indptr_h,
-                               const std::vector<int64_t>& kv_len) {
+template <class PP>
+void plan_prefill_order(PP& p, int32_t batch, const int32_t* qo_indptr_h, const std::vector<int64_t>& kv_len) {
   p.n_items = 0;
   if (batch >= 65536) return;
   int64_t pairs = 0;
   for (int32_t i = 0; i < batch; ++i) pairs += ceil_div(qo_indptr_h[i + 1] - qo_indptr_h[i], p.q_per_wg);
-  if (pairs > fi::kPrefillOrderMax) return;
+  if (pairs > PP::kOrderMax) return;
   std::vector<std::pair<int64_t, uint32_t>> items;  // (tiles, request << 16 | block)
   items.reserve((size_t)pairs);
   for (int32_t i = 0; i < batch; ++i) {
@@ -428,13 +483,13 @@ fi_status check_queries(const char* fn, const void* q, void* o, int32_t batch, c
   return FI_OK;
 }
 
-// Common tail of the prefill calls: work-group shape, scales, dispatch order
-// and the launch.  p already holds the tensors and the K/V addressing.
-fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi_dtype kv_dtype,
-                             fi_dtype o_dtype, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                             int32_t head_dim, int32_t causal, int64_t max_qo, const int32_t* qo_indptr_h,
-                             const std::vector<int64_t>& kv_len, float sm_scale, float k_scale, float v_scale,
-                             bool ragged, hipStream_t stream) {
+// Work-group shape, scales and dispatch order of a prefill batch; p already
+// holds the tensors and the K/V addressing.
+template <class PP>
+fi_status plan_prefill(const char* fn, PP& p, fi_dtype kv_dtype, int32_t batch, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t causal, int64_t max_qo,
+                       const int32_t* qo_indptr_h, const std::vector<int64_t>& kv_len, float sm_scale, float k_scale,
+                       float v_scale) {
   p.num_qo_heads = num_qo_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_qo_heads / num_kv_heads;
@@ -453,6 +508,18 @@ fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi
   if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
                                        (long long)max_qo, 65535 * p.q_per_wg);
   plan_prefill_order(p, batch, qo_indptr_h, kv_len);
+  return FI_OK;
+}
+
+// Common tail of the prefill calls: the plan, then the launch.
+fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi_dtype kv_dtype,
+                             fi_dtype o_dtype, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t causal, int64_t max_qo, const int32_t* qo_indptr_h,
+                             const std::vector<int64_t>& kv_len, float sm_scale, float k_scale, float v_scale,
+                             bool ragged, hipStream_t stream) {
+  fi_status st = plan_prefill(fn, p, kv_dtype, batch, num_qo_heads, num_kv_heads, head_dim, causal, max_qo,
+                              qo_indptr_h, kv_len, sm_scale, k_scale, v_scale);
+  if (st != FI_OK) return st;
   hipError_t err = fi::launch_prefill(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, ragged, stream);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));
   return FI_OK;
@@ -692,6 +759,128 @@ fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_s
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * q_scale, kv->v_scale, false,
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+// Prefill and decode batches in one launch.  Both phases must agree on the
+// query, output and KV dtypes and on the head layout (they run one kernel);
+// each has its own page table and scales.  The prefill phase takes the
+// prefill rules (a 2-byte KV equal to q), and so does the decode phase, as the
+// pages' POD entry points do.
+fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const int32_t* qo_indptr_h, int32_t batch_p,
+                             const fi_paged_kv* kv_p, int32_t causal, void* o_p, float* lse_p, const void* q_d,
+                             int32_t batch_d, const fi_paged_kv* kv_d, void* o_d, float* lse_d, fi_dtype q_dtype,
+                             fi_dtype o_dtype, int32_t num_qo_heads, float sm_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  static const char* fn = "fi_batch_pod_paged";
+  static const char* fn_d = "fi_batch_pod_paged (decode phase)";
+  if (!kv_p || !kv_d) return fail(FI_E_ARG, fn, "kv_p and kv_d must not be NULL");
+  fi_status st = check_dtypes(fn, q_dtype, &o_dtype, kv_p->k_dtype, kv_p->v_dtype, true);
+  if (st != FI_OK) return st;
+  fi_dtype o_d_dtype = o_dtype;
+  if ((st = check_dtypes(fn_d, q_dtype, &o_d_dtype, kv_d->k_dtype, kv_d->v_dtype, true)) != FI_OK) return st;
+  if (kv_d->k_dtype != kv_p->k_dtype)
+    return fail(FI_E_DTYPE, fn, "the prefill phase's KV cache has dtype %s but the decode phase's has dtype %s; both "
+                "phases of one call run one kernel over one KV dtype", dtype_name(kv_p->k_dtype),
+                dtype_name(kv_d->k_dtype));
+  if (batch_p < 0 || batch_d < 0)
+    return fail(FI_E_SHAPE, fn, "batch sizes must not be negative (prefill %d, decode %d)", batch_p, batch_d);
+  if ((st = check_heads(fn, num_qo_heads, kv_p->num_kv_heads, kv_p->head_dim)) != FI_OK) return st;
+  if (kv_d->num_kv_heads != kv_p->num_kv_heads || kv_d->head_dim != kv_p->head_dim)
+    return fail(FI_E_SHAPE, fn, "the decode phase's cache has %d kv heads of head_dim %d but the prefill phase's has "
+                "%d of head_dim %d; both phases share the head layout", kv_d->num_kv_heads, kv_d->head_dim,
+                kv_p->num_kv_heads, kv_p->head_dim);
+  if (batch_p > 0 && (!qo_indptr || !qo_indptr_h)) return fail(FI_E_ARG, fn, "qo_indptr and qo_indptr_h must not be NULL");
+  if ((st = check_scales(fn, kv_p->k_scale, kv_p->v_scale, sm_scale)) != FI_OK) return st;
+  if ((st = check_scales(fn_d, kv_d->k_scale, kv_d->v_scale, sm_scale)) != FI_OK) return st;
+  int64_t max_kv_p = 0, total_kv_p = 0, max_kv_d = 0, total_kv_d = 0;
+  if ((st = check_paged(fn, batch_p, kv_p, &max_kv_p, &total_kv_p)) != FI_OK) return st;
+  if ((st = check_paged(fn_d, batch_d, kv_d, &max_kv_d, &total_kv_d)) != FI_OK) return st;
+  int64_t max_qo = 0;
+  if ((st = check_queries(fn, q_p, o_p, batch_p, qo_indptr, qo_indptr_h, &max_qo)) != FI_OK) return st;
+  if (batch_d > 0) {
+    if (!q_d || !o_d) return fail(FI_E_ARG, fn_d, "q and o must not be NULL");
+    if (!aligned16(q_d) || !aligned16(o_d)) return fail(FI_E_ARG, fn_d, "q and o must be 16-byte aligned");
+  }
+  const int eb = elem_bytes(kv_p->k_dtype);
+  const int32_t hd = kv_p->head_dim;
+  fi::PodParams pp{};
+  // prefill phase: every (request, query block) pair in the dispatch order
+  if (batch_p > 0 && max_qo > 0) {
+    fi::PrefillParamsT<fi::kPodOrderMax>& f = pp.pf;
+    f.q = q_p;
+    f.o = o_p;
+    f.lse = lse_p;
+    f.k = reinterpret_cast<const uint8_t*>(kv_p->k);
+    f.v = reinterpret_cast<const uint8_t*>(kv_p->v);
+    f.sp = kv_p->stride_page * eb;
+    f.st = kv_p->stride_token * eb;
+    f.sh = kv_p->stride_head * eb;
+    f.qo_indptr = qo_indptr;
+    f.indptr = kv_p->indptr;
+    f.indices = kv_p->indices;
+    f.last_page_len = kv_p->last_page_len;
+    f.page_shift = ilog2(kv_p->page_size);
+    f.page_size = kv_p->page_size;
+    std::vector<int64_t> kv_len((size_t)batch_p);
+    for (int32_t i = 0; i < batch_p; ++i) {
+      const int64_t np = kv_p->indptr_h[i + 1] - kv_p->indptr_h[i];
+      kv_len[i] = np > 0 ? (np - 1) * kv_p->page_size + kv_p->last_page_len_h[i] : 0;
+    }
+    if ((st = plan_prefill(fn, f, kv_p->k_dtype, batch_p, num_qo_heads, kv_p->num_kv_heads, hd, causal, max_qo,
+                           qo_indptr_h, kv_len, sm_scale, kv_p->k_scale, kv_p->v_scale)) != FI_OK)
+      return st;
+    if (f.n_items == 0)
+      return fail(FI_E_SHAPE, fn, "the prefill phase has more than %d (request, query block) pairs of %d queries, the "
+                  "most one launch's arguments carry; fi_batch_prefill_paged has no such limit", fi::kPodOrderMax,
+                  f.q_per_wg);
+    pp.n_prefill_wg = f.n_items * kv_p->num_kv_heads * (f.group / f.heads_per_wg);
+  }
+  // decode phase: balanced slices over 8-wave workgroups, two per CU unless
+  // FI_POD_DECODE_WG names a count
+  bool merge = false;
+  if (batch_d > 0) {
+    fi::DecodeParamsT<fi::kPodPrefixMax>& d = pp.dc;
+    d.q = q_d;
+    d.o = o_d;
+    d.lse = lse_d;
+    d.k = reinterpret_cast<const uint8_t*>(kv_d->k);
+    d.v = reinterpret_cast<const uint8_t*>(kv_d->v);
+    d.sp = kv_d->stride_page * eb;
+    d.st = kv_d->stride_token * eb;
+    d.sh = kv_d->stride_head * eb;
+    d.indptr = kv_d->indptr;
+    d.indices = kv_d->indices;
+    d.last_page_len = kv_d->last_page_len;
+    d.page_shift = ilog2(kv_d->page_size);
+    d.page_size = kv_d->page_size;
+    d.num_qo_heads = num_qo_heads;
+    d.num_kv_heads = kv_d->num_kv_heads;
+    d.group = num_qo_heads / kv_d->num_kv_heads;
+    int slots = 2 * fi::device_cus();
+    if (const char* env = std::getenv("FI_POD_DECODE_WG")) {
+      const long n = std::strtol(env, nullptr, 10);
+      if (n > 0 && n < (1 << 20)) slots = (int)n;
+    }
+    size_t need = 0;
+    if ((st = plan_decode(fn_d, d, fi::kPodDecodeWaves, std::max(slots, 1), q_dtype, kv_d->k_dtype, o_dtype, batch_d,
+                          hd, kv_d->indptr_h, kv_d->last_page_len_h, kv_d->page_size, max_kv_d, total_kv_d,
+                          workspace != nullptr, &merge, &need)) != FI_OK)
+      return st;
+    if ((st = decode_workspace(fn_d, need, &workspace, workspace_bytes, false, batch_d)) != FI_OK) return st;
+    finish_decode(d, kv_d->k_dtype, batch_d, hd, sm_scale, kv_d->k_scale, kv_d->v_scale, workspace, need);
+    const int64_t nwg = decode_workgroups(d, batch_d);
+    if (nwg + pp.n_prefill_wg > 0x7fffffff) return fail(FI_E_SHAPE, fn, "the launch needs more than 2^31 workgroups");
+    pp.n_decode_wg = (int32_t)nwg;
+  }
+  if (pp.n_prefill_wg + (int64_t)pp.n_decode_wg == 0) return FI_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = fi::launch_pod(pp, q_dtype, kv_p->k_dtype, o_dtype, hd, s);
+  if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill + decode kernel launch failed: %s", hipGetErrorString(err));
+  if (merge) {
+    err = launch_decode_merge(pp.dc, o_dtype, batch_d, hd, s);
+    if (err != hipSuccess) return fail(FI_E_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(err));
+  }
+  return FI_OK;
 }
 
 }  // extern "C"

@@ -18,7 +18,10 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kBalancedMaxBatch = 1024; // largest batch the balanced decode split handles
 constexpr int kDecodePrefixMax = 768;   // largest batch whose token prefix sums travel in the kernel arguments
 
-struct DecodeParams {
+// NPRE: capacity of the token prefix sums carried in the arguments
+template <int NPRE>
+struct DecodeParamsT {
+  static constexpr int kPrefixMax = NPRE;
   const void* q;          // [tokens, Hqo, D]
   void* o;                // [tokens, Hqo, D]
   float* lse;             // [tokens, Hqo] or null
@@ -56,8 +59,9 @@ struct DecodeParams {
   // (pre[i] = tokens of requests < i, i <= batch) when they fit; else
   // pre_n = 0 and every workgroup scans the device page table itself
   int32_t pre_n;
-  int32_t pre[kDecodePrefixMax + 1];
+  int32_t pre[NPRE + 1];
 };
+using DecodeParams = DecodeParamsT<kDecodePrefixMax>;
 
 struct MergeParams {
   void* o;
@@ -79,7 +83,10 @@ constexpr int kPrefillWaves = 8;
 // in the kernel arguments (4 bytes each).
 constexpr int kPrefillOrderMax = 768;
 
-struct PrefillParams {
+// NORD: capacity of the dispatch order carried in the arguments
+template <int NORD>
+struct PrefillParamsT {
+  static constexpr int kOrderMax = NORD;
   const void* q;          // [total_q, Hqo, D]
   void* o;
   float* lse;
@@ -108,8 +115,25 @@ struct PrefillParams {
   // heads * head groups)] = request << 16 | query block, listed heaviest
   // first; otherwise x = (request, kv head, head group) and y = query block.
   int32_t n_items;
-  uint32_t order[kPrefillOrderMax];
+  uint32_t order[NORD];
 };
+using PrefillParams = PrefillParamsT<kPrefillOrderMax>;
+
+// One launch over a prefill batch and a decode batch ("POD"): workgroups
+// [0, n_prefill_wg) run prefill work items in the heaviest-first order, the
+// next n_decode_wg run decode slices with kPodDecodeWaves waves each.  The
+// two plans share the kernel-argument budget of one launch, so their lists
+// are shorter than the separate calls'.
+constexpr int kPodDecodeWaves = 8;
+constexpr int kPodOrderMax = 448;
+constexpr int kPodPrefixMax = 320;
+struct PodParams {
+  PrefillParamsT<kPodOrderMax> pf;
+  DecodeParamsT<kPodPrefixMax> dc;
+  int32_t n_prefill_wg;
+  int32_t n_decode_wg;
+};
+static_assert(sizeof(PodParams) <= 4096, "POD kernel arguments exceed 4 KB");
 
 // Kernel launchers (defined in the .hip translation units).  They return the
 // hipError_t of the launch.
@@ -123,6 +147,8 @@ int device_cus();  // compute units of the current device (0 on error), cached
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
                           bool ragged, hipStream_t s);
 hipError_t launch_fp8_widen(const uint8_t* codes, int64_t n, int src_fmt, int dst_fmt, void* out, hipStream_t s);
+// POD: q in {f16, bf16}, KV q's 2-byte type or any fp8, paged prefill with a 2-byte query
+hipError_t launch_pod(const PodParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, hipStream_t s);
 
 // Split-KV scratch of the allocation-free decode call: a file-scope device
 // array of kDecodeScratchBytes in the decode translation unit, one copy per

@@ -19,7 +19,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfi.so")
+# FI_LIB_PATH names another build of the same library (the sanitizer build's
+# CPU checks use it); by default the in-tree libfi.so.
+LIB_PATH = os.environ.get("FI_LIB_PATH") or os.path.join(_HERE, "libfi.so")
 
 # fi_dtype
 DTYPES = {
@@ -37,7 +39,7 @@ STATUS = {0: "FI_OK", 1: "FI_E_DTYPE", 2: "FI_E_SHAPE", 3: "FI_E_ARG", 4: "FI_E_
 EXPORTS = ("fi_last_error", "fi_decode_workspace_bytes", "fi_batch_decode_paged", "fi_batch_decode_paged_fp8q",
            "fi_batch_prefill_paged", "fi_batch_prefill_paged_fp8q", "fi_batch_prefill_ragged",
            "fi_batch_prefill_ragged_fp8q", "fi_single_prefill", "fi_single_prefill_fp8q", "fi_single_decode",
-           "fi_fp8_widen", "fi_batch_decode_paged_noalloc")
+           "fi_fp8_widen", "fi_batch_decode_paged_noalloc", "fi_batch_pod_paged")
 DECODE_SCRATCH_BYTES = 32 << 20  # FI_DECODE_SCRATCH_BYTES
 
 
@@ -102,6 +104,9 @@ def lib() -> ctypes.CDLL:
     L.fi_batch_decode_paged.argtypes = [vp, en, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz, vp]
     L.fi_batch_decode_paged_noalloc.restype = en
     L.fi_batch_decode_paged_noalloc.argtypes = [vp, en, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp]
+    L.fi_batch_pod_paged.restype = en
+    L.fi_batch_pod_paged.argtypes = [vp, vp, vp, i32, ctypes.POINTER(PagedKV), i32, vp, vp, vp, i32,
+                                     ctypes.POINTER(PagedKV), vp, vp, en, en, i32, f32, vp, sz, vp]
     L.fi_batch_decode_paged_fp8q.restype = en
     L.fi_batch_decode_paged_fp8q.argtypes = [vp, en, f32, i32, i32, ctypes.POINTER(PagedKV), vp, en, vp, f32, vp, sz,
                                              vp]
@@ -182,7 +187,10 @@ def make_paged_kv(k_pool, v_pool, indptr, indices, last_page_len, *, k_scale=1.0
                   k_dtype=None, v_dtype=None, indptr_h=None, last_page_len_h=None):
     """Describe a paged cache.  Pools are [num_pages, page_size, H_kv, head_dim]
     tensors with a contiguous last dimension; raw fp8 may be passed as uint8
-    with kv_dtype naming the format.  Returns (struct, keepalive)."""
+    with kv_dtype naming the format.  Returns (struct, keepalive): the struct
+    holds raw pointers, and keepalive holds every tensor they point at (the
+    pools, the device page table and the host copies), so the caller keeps
+    keepalive for as long as the struct is used."""
     if tuple(k_pool.stride()) != tuple(v_pool.stride()) or k_pool.shape != v_pool.shape:
         raise FiValueError(2, "k and v pools must have the same shape and strides")
     kd = k_dtype if k_dtype is not None else (kv_dtype if kv_dtype is not None else k_pool.dtype)
@@ -198,7 +206,7 @@ def make_paged_kv(k_pool, v_pool, indptr, indices, last_page_len, *, k_scale=1.0
     s.indptr, s.indices, s.last_page_len = _ptr(indptr), _ptr(indices), _ptr(last_page_len)
     s.indptr_h, s.last_page_len_h = ih.data_ptr(), lh.data_ptr()
     s.k_scale, s.v_scale = float(k_scale), float(v_scale)
-    return s, (ih, lh)
+    return s, (ih, lh, k_pool, v_pool, indptr, indices, last_page_len)
 
 
 def fi_batch_decode_paged(q, kv: PagedKV, o, *, q_dtype=None, o_dtype=None, lse=None, sm_scale=0.0,
@@ -257,6 +265,26 @@ def fi_batch_prefill_paged(q, qo_indptr, kv: PagedKV, o, *, causal=True, q_dtype
     return o
 
 
+def fi_batch_pod_paged(q_p, qo_indptr, kv_p: PagedKV, o_p, q_d, kv_d: PagedKV, o_d, *, causal=True, lse_p=None,
+                       lse_d=None, q_dtype=None, o_dtype=None, sm_scale=0.0, qo_indptr_h=None, batch_p=None,
+                       batch_d=None, num_qo_heads=None, workspace=None, workspace_bytes=None, stream=None):
+    """One launch over a prefill batch (q_p / o_p [total_q, H_qo, D], qo_indptr
+    [batch_p+1] on the device) and a decode batch (q_d / o_d [batch_d, H_qo, D])."""
+    qh = _host_i32(qo_indptr_h if qo_indptr_h is not None else qo_indptr)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    qd = q_dtype if q_dtype is not None else (q_p.dtype if q_p is not None else q_d.dtype)
+    od = o_dtype if o_dtype is not None else (o_p.dtype if o_p is not None else o_d.dtype)
+    hq = num_qo_heads if num_qo_heads is not None else (q_p.shape[1] if q_p is not None else q_d.shape[1])
+    st = lib().fi_batch_pod_paged(
+        _ptr(q_p), _ptr(qo_indptr), qh.data_ptr(), int(batch_p if batch_p is not None else qh.numel() - 1),
+        ctypes.byref(kv_p), 1 if causal else 0, _ptr(o_p), _ptr(lse_p), _ptr(q_d),
+        int(batch_d if batch_d is not None else q_d.shape[0]), ctypes.byref(kv_d), _ptr(o_d), _ptr(lse_d), _dt(qd),
+        _dt(od), int(hq), float(sm_scale), _ptr(workspace), int(workspace_bytes), _stream(stream, q_p, q_d, o_p, o_d))
+    check(st)
+    return o_p, o_d
+
+
 def fi_batch_prefill_paged_fp8q(q, qo_indptr, kv: PagedKV, o, *, q_dtype, o_dtype=None, q_scale=1.0, causal=True,
                                 pv_fp8=False, lse=None, sm_scale=0.0, qo_indptr_h=None, batch=None, num_qo_heads=None,
                                 stream=None):
@@ -277,7 +305,8 @@ def make_ragged_kv(k, v, indptr, *, k_scale=1.0, v_scale=1.0, kv_dtype=None, k_d
     """Describe a ragged K/V: k and v are [num_tokens, H_kv, head_dim] tensors
     with a contiguous last dimension, request i owning rows indptr[i] ..
     indptr[i+1]-1; raw fp8 may be passed as uint8 with kv_dtype naming the
-    format.  Returns (struct, keepalive)."""
+    format.  Returns (struct, keepalive); keepalive holds every tensor the
+    struct points at."""
     if tuple(k.stride()) != tuple(v.stride()) or k.shape != v.shape:
         raise FiValueError(2, "k and v must have the same shape and strides")
     kd = k_dtype if k_dtype is not None else (kv_dtype if kv_dtype is not None else k.dtype)
@@ -290,7 +319,7 @@ def make_ragged_kv(k, v, indptr, *, k_scale=1.0, v_scale=1.0, kv_dtype=None, k_d
     s.num_tokens, s.num_kv_heads, s.head_dim = int(k.shape[0]), int(k.shape[1]), int(k.shape[2])
     s.indptr, s.indptr_h = _ptr(indptr), ih.data_ptr()
     s.k_scale, s.v_scale = float(k_scale), float(v_scale)
-    return s, (ih,)
+    return s, (ih, k, v, indptr)
 
 
 def fi_batch_prefill_ragged(q, qo_indptr, kv: RaggedKV, o, *, causal=True, q_dtype=None, o_dtype=None, lse=None,

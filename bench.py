@@ -236,11 +236,11 @@ def run_prefill_bench(steps, warmup, ragged=False, fp8q=False, pv_fp8=False, cop
 
 
 def kernel_source_hash(kind: str) -> str:
-    """sha256 over the sources that define a kernel (its .hip file and the
-    shared device and internal headers)."""
+    """sha256 over the sources that define a kernel (its .hip file, its body
+    header and the shared device and internal headers)."""
     csrc = os.path.join(ROOT, "attention_paged_fp8_amd", "csrc")
     h = hashlib.sha256()
-    for name in (f"fi_{kind}.hip", "fi_device.hpp", "fi_internal.h"):
+    for name in (f"fi_{kind}.hip", f"fi_{kind}_body.hpp", "fi_device.hpp", "fi_internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -304,6 +304,64 @@ def decode_extra(steps, warmup):
     return out
 
 
+def run_pod_bench(steps, warmup, copies=3):
+    """The mixed batch -- the causal-prefill workload (16 requests) and the
+    batch-decode shapes with an f16 query over e4m3 (64 requests) -- three
+    ways: one fi_batch_pod_paged call; the two separate calls back to back on
+    one stream; the two calls on two streams of default priority, joined.
+    HIP events on the launch stream around each whole step; `copies` full
+    input sets rotated.  Returns medians in microseconds."""
+    import torch
+
+    from attention_paged_fp8_amd import fi
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    wp = make_workload("causal_prefill")
+    wd = make_workload("dtype_decode", kvd="e4m3")
+    main = torch.cuda.current_stream(dev)
+    sp, sd = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    nws = fi.fi_decode_workspace_bytes(len(wd["kv_lens"]), wd["num_qo_heads"], wd["head_dim"], int(wd["kv_lens"].max()))
+    sets = []
+    for _ in range(copies):
+        qp, ip, kvp, kp = _upload(wp, dev, 1)
+        qd, idd, kvd, kd = _upload(wd, dev, 1)
+        op = torch.empty(qp.shape, dtype=torch.float16, device=dev)
+        lp = torch.empty(qp.shape[:2], dtype=torch.float32, device=dev)
+        od = torch.empty(qd.shape, dtype=torch.float16, device=dev)
+        ld = torch.empty(qd.shape[:2], dtype=torch.float32, device=dev)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        # the PagedKV structs point at both page tables (ip, idd): keep them with the set
+        sets.append((qp, ip, kvp[0], op, lp, qd, kvd[0], od, ld, ws, kp, kd, idd))
+
+    def pod(i):
+        qp, ip, kvp, op, lp, qd, kvd, od, ld, ws = sets[i % copies][:10]
+        fi.fi_batch_pod_paged(qp, ip["qo_indptr"], kvp, op, qd, kvd, od, causal=True, lse_p=lp, lse_d=ld,
+                              qo_indptr_h=wp["qo_indptr"], workspace=ws, stream=main)
+
+    def serial(i, st_p=None, st_d=None):
+        qp, ip, kvp, op, lp, qd, kvd, od, ld, ws = sets[i % copies][:10]
+        fi.fi_batch_prefill_paged(qp, ip["qo_indptr"], kvp, op, causal=True, lse=lp, qo_indptr_h=wp["qo_indptr"],
+                                  stream=st_p or main)
+        fi.fi_batch_decode_paged(qd, kvd, od, lse=ld, workspace=ws, stream=st_d or main)
+
+    def two_streams(i):
+        sp.wait_stream(main)
+        sd.wait_stream(main)
+        serial(i, sp, sd)
+        main.wait_stream(sp)
+        main.wait_stream(sd)
+
+    out = {}
+    for name, fn in (("pod_one_launch", pod), ("two_calls_one_stream", serial), ("two_calls_two_streams", two_streams)):
+        _, ev = _time_calls(fn, copies, steps, warmup, main)
+        out[name] = round(float(np.median(ev)) * 1e3, 2)
+    torch.cuda.synchronize()
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_copy_calibration(mb: int, reps: int = 5):
     """A plain device-to-device copy of `mb` MiB, `reps` times: the reference
     the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -354,7 +412,7 @@ def host_info() -> dict:
     return dict(cpu_model=model, nproc=os.cpu_count(), cpus_available=avail, threads=threads, blas=blas)
 
 
-def cpu_baseline(wd, runs: int = 3, prefill_requests=(0, 1, 2, 3)):
+def cpu_baseline(wd, runs: int = 3, prefill_requests=tuple(range(16))):
     """The float64 oracle on the host's cores (BLAS threads = the CPU share
     this process has: OMP_NUM_THREADS when set, else every available core),
     median of `runs` runs of each sample: the whole batch-decode workload
@@ -402,7 +460,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-runs", type=int, default=3, help="runs of each oracle sample (median reported)")
-    ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "prefill", "pod"), default="all",
                     help="run one path only (for per-kernel counter passes)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -429,6 +487,8 @@ def main():
     w, eager_ms, ev, graph_ms = make_workload("batch_decode"), float("nan"), np.array([float("nan")]), float("nan")
     if args.only in ("all", "decode"):
         w, eager_ms, ev, graph_ms = run_decode_bench(args.steps, args.warmup, args.copies, graph=True)
+    elif args.only == "pod":
+        graph_ms = None
     nbytes = decode_bytes(w)
     # whole-job rate: the timed steps replayed as one captured graph (eager calls if capture failed)
     graphed = graph_ms is not None
@@ -476,13 +536,21 @@ def main():
             print(f"# prefill, fp8 query and fp8 P V: events median {g_ms * 1e3:.1f} us -> "
                   f"{flops / (g_ms * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    extra, copy_gbs = None, None
+    extra, copy_gbs, pod = None, None, None
+    if args.only in ("all", "pod") and not args.no_extra:
+        pod = run_pod_bench(args.prefill_steps, 3)
+        pod["workload"] = ("causal_prefill_b16_qo256-1024_prefix0-2048_h32-8_d128_page16_e4m3_f16 + "
+                           "dtype_decode_b64_kv512-4096_h32-8_d128_page16_f16q_kv_e4m3")
+        pod["unit"] = "us (median of HIP events around the whole step)"
+        print(f"# mixed prefill + decode batch: one POD launch {pod['pod_one_launch']} us, two calls on one stream "
+              f"{pod['two_calls_one_stream']} us, on two streams {pod['two_calls_two_streams']} us", file=sys.stderr,
+              flush=True)
     if args.only == "all" and not args.no_extra:
         extra = decode_extra(max(5, args.steps // 2), 3)
         copy_gbs = round(copy_bandwidth(), 1)
         print(f"# plain device copy: {copy_gbs} GB/s", file=sys.stderr, flush=True)
 
-    cpu = None if (args.no_cpu or args.only == "prefill") else cpu_baseline(w, args.cpu_runs)
+    cpu = None if (args.no_cpu or args.only in ("prefill", "pod")) else cpu_baseline(w, args.cpu_runs)
     if cpu is not None and prefill is not None:
         prefill["cpu_baseline"] = cpu["prefill"]
     if cpu is not None:
@@ -520,6 +588,7 @@ def main():
         },
         "prefill": prefill,
         "decode_other": extra,
+        "pod": pod,
         "copy_gbs": copy_gbs,
         "cpu_baseline": cpu,
     }

@@ -214,6 +214,39 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
                                  const fi_paged_kv* kv, int32_t causal, void* o, fi_dtype o_dtype, float* lse,
                                  float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* A prefill batch and a decode batch in one launch ("POD"; [C] Refusals and
+ * Architecture / design notes: the POD and batch-POD run entry points beside
+ * prefill and decode, with the prefill dtype rules and the k/v check).
+ *   prefill phase: q_p, qo_indptr / qo_indptr_h, batch_p, kv_p, causal, o_p,
+ *     lse_p -- as fi_batch_prefill_paged;
+ *   decode phase: q_d, batch_d, kv_d, o_d, lse_d -- as fi_batch_decode_paged,
+ *     one query per request;
+ *   q_dtype, o_dtype (FI_DTYPE_DEFAULT = q_dtype), num_qo_heads and sm_scale
+ *     are shared, as is one KV dtype: kv_p and kv_d must have the same dtype,
+ *     num_kv_heads and head_dim (one kernel runs both phases; a mismatch
+ *     between the phases is refused, never reinterpreted), and a 2-byte KV
+ *     must equal q in both phases ([C]: "on prefill and POD").  fp8 KV (OCP
+ *     or fnuz) is widened on load as in the other calls.  kv_p and kv_d may
+ *     describe the same pools with different page tables, or different pools;
+ *     each phase has its own k_scale / v_scale.
+ *   workspace / workspace_bytes: the decode phase's split-KV scratch, as for
+ *     fi_batch_decode_paged (NULL: no split).
+ * Results are those of the two separate calls (the prefill phase bit for bit;
+ * the decode phase within tolerance: it is cut into slices for 8-wave
+ * workgroups instead of the decode kernel's 4).  The prefill phase may hold at
+ * most 448 (request, block of 256 / heads_per_group query rows) pairs, which
+ * the launch's arguments carry; more is refused with FI_E_SHAPE.  Checks run
+ * in the order of fi_batch_prefill_paged for the prefill phase, then the same
+ * for the decode phase (its sentences name "(decode phase)"), then the
+ * cross-phase dtype and head checks, shapes and pointers, then workspace.
+ * Environment: FI_POD_DECODE_WG = a positive count of decode workgroups to
+ * cut the decode phase into (default two per compute unit). */
+fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const int32_t* qo_indptr_h, int32_t batch_p,
+                             const fi_paged_kv* kv_p, int32_t causal, void* o_p, float* lse_p, const void* q_d,
+                             int32_t batch_d, const fi_paged_kv* kv_d, void* o_d, float* lse_d, fi_dtype q_dtype,
+                             fi_dtype o_dtype, int32_t num_qo_heads, float sm_scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Batched prefill over the paged cache with an fp8 query ([A] review
  * comments: q_scale folded into sm_scale for the first product; [A]
  * Walkthrough and review comments: an fp8 input gives a float16 or bfloat16

@@ -45,7 +45,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(fi.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -452,6 +452,50 @@ def test_noalloc_refuses_a_split_beyond_its_scratch(L, monkeypatch):
     st = L.fi_batch_decode_paged_noalloc(fake, fi.DTYPES["f16"], 2, 4, ctypes.byref(kv2), fake, fi.DTYPES["e4m3"],
                                          None, 0.0, None)
     assert st == 1 and "an fp8 output is not supported" in _err(L)
+
+
+def _pod(L, kv_p, kv_d, q="f16", o="default", hq=4, batch_p=2, batch_d=2, ptrs=False, qo=(0, 3, 7)):
+    qo = np.asarray(qo, np.int32)
+    fake = 0x10000 if ptrs else None
+    return L.fi_batch_pod_paged(fake, fake, qo.ctypes.data, batch_p, ctypes.byref(kv_p), 1, fake, None, fake, batch_d,
+                                ctypes.byref(kv_d), fake, None, fi.DTYPES[q], fi.DTYPES[o], hq, 0.0, None, 0, None)
+
+
+@no_gpu
+def test_pod_refusals(L):
+    """The POD call: the prefill rules on both phases (sentences naming the
+    decode phase when it is the decode phase's), then the cross-phase checks
+    -- one KV dtype and one head layout for both phases, never reinterpreted
+    ("fp8 KV cache in the in-tree prefill kernel", review comments on POD
+    cross-phase dtype validation) -- then shapes and the argument budget."""
+    kv, keep = _kv(ptrs=True)
+    assert _pod(L, kv, kv, q="e4m3", ptrs=True) == 1 and "q has dtype float8_e4m3fn" in _err(L)
+    assert _pod(L, kv, kv, o="e5m2", ptrs=True) == 1 and "an fp8 output is not supported" in _err(L)
+    kvm, keepm = _kv("e4m3", "e5m2", ptrs=True)
+    assert _pod(L, kvm, kv, ptrs=True) == 1 and _err(L).startswith("fi_batch_pod_paged: k has dtype")
+    assert _pod(L, kv, kvm, ptrs=True) == 1
+    assert _err(L).startswith("fi_batch_pod_paged (decode phase): k has dtype float8_e4m3fn but v has dtype float8_e5m2")
+    kvb, keepb = _kv("bf16", ptrs=True)
+    assert _pod(L, kvb, kvb, q="f16", ptrs=True) == 1 and "prefill needs a 2-byte KV cache of the query's dtype" in _err(L)
+    kvi, keepi = _kv("i8", ptrs=True)
+    assert _pod(L, kv, kvi, ptrs=True) == 1 and "(decode phase): KV cache has dtype int8" in _err(L)
+    kv5, keep5 = _kv("e5m2", ptrs=True)
+    assert _pod(L, kv, kv5, ptrs=True) == 1
+    assert "prefill phase's KV cache has dtype float8_e4m3fn but the decode phase's has dtype float8_e5m2" in _err(L)
+    kvh, keeph = _kv(ptrs=True, hkv=4)
+    assert _pod(L, kv, kvh, ptrs=True) == 2 and "both phases share the head layout" in _err(L)
+    assert _pod(L, kv, kv, hq=3, ptrs=True) == 2 and "not a multiple" in _err(L)
+    assert _pod(L, kv, kv, batch_p=-1, ptrs=True) == 2
+    kvl, keepl = _kv(ptrs=True, lpl=[5, 0])
+    assert _pod(L, kv, kvl, ptrs=True) == 3 and "(decode phase): last_page_len[1]=0" in _err(L)
+    assert _pod(L, kv, kv, ptrs=False) == 3  # NULL pointers
+    # more (request, query block) pairs than one launch's arguments carry:
+    # 449 requests of 40 queries (4 q heads, 1 kv head group -> 64 rows per pair)
+    lens = np.full(449, 40)
+    kvp, keepp = _kv(ptrs=True, lens=lens)
+    qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert _pod(L, kvp, kv, batch_p=449, ptrs=True, qo=qo) == 2 and "at most 448" not in _err(L)
+    assert "more than 448 (request, query block) pairs" in _err(L), _err(L)
 
 
 @no_gpu

@@ -70,3 +70,38 @@ def test_binding_matches_prototype(name):
     want = [_kind(p) for p in PROTOS[name]]
     got = [_ctype_kind(t) for t in (fn.argtypes or [])]
     assert got == want, f"{name}: binding {got} against header {want}"
+
+
+def test_keepalive_holds_every_tensor_the_struct_points_at():
+    """make_paged_kv / make_ragged_kv return raw pointers in a struct; their
+    keepalive must hold the pools and the device page table too, so a caller
+    that keeps it cannot end up with pointers to freed memory (a page table
+    freed under a live struct reads garbage page ids)."""
+    import gc
+    import weakref
+
+    import numpy as np
+    import torch
+
+    def tensors():
+        k = torch.zeros((4, 16, 2, 64), dtype=torch.uint8)
+        return k, k.clone(), torch.tensor([0, 2, 4], dtype=torch.int32), torch.arange(4, dtype=torch.int32), \
+            torch.tensor([16, 3], dtype=torch.int32)
+
+    k, v, ip, ix, lp = tensors()
+    refs = [weakref.ref(t) for t in (k, v, ip, ix, lp)]
+    s, keep = fi.make_paged_kv(k, v, ip, ix, lp, kv_dtype="e4m3")
+    del k, v, ip, ix, lp
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert s.indices == refs[3]().data_ptr() and s.k == refs[0]().data_ptr()
+    del keep
+    gc.collect()
+    assert all(r() is None for r in refs)
+    k, v, ind = torch.zeros((7, 2, 64), dtype=torch.uint8), torch.zeros((7, 2, 64), dtype=torch.uint8), \
+        torch.tensor([0, 7], dtype=torch.int32)
+    refs = [weakref.ref(t) for t in (k, v, ind)]
+    s, keep = fi.make_ragged_kv(k, v, ind, kv_dtype="e4m3")
+    del k, v, ind
+    gc.collect()
+    assert all(r() is not None for r in refs)
