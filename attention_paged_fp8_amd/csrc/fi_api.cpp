@@ -856,7 +856,32 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
     d.num_qo_heads = num_qo_heads;
     d.num_kv_heads = kv_d->num_kv_heads;
     d.group = num_qo_heads / kv_d->num_kv_heads;
-    int slots = 2 * fi::device_cus();
+    // Decode slices first, on few workgroups: the decode stream needs HBM
+    // bandwidth rather than CUs, so a fraction of the CUs streams it while the
+    // rest start the prefill items, which then fill the CUs the decode
+    // workgroups leave.  The fraction balances the two phases' estimated
+    // durations: decode bytes at kPodDecodeWgRate per 8-wave workgroup against
+    // prefill flops at kPodPrefillCuRate per CU (both measured on MI355X under
+    // sustained load: the causal-prefill workload at ~826 TFLOP/s over 256 CUs;
+    // a lone decode workgroup streams ~20 GB/s).  A decode-only call takes two
+    // workgroups per CU.  FI_POD_DECODE_WG overrides the count.
+    constexpr double kPodPrefillCuRate = 3.2e12, kPodDecodeWgRate = 20e9;
+    const int cus = std::max(1, fi::device_cus());
+    int slots = 2 * cus;
+    if (pp.n_prefill_wg > 0) {
+      double flops = 0;
+      for (int32_t i = 0; i < batch_p; ++i) {
+        const int64_t qo = qo_indptr_h[i + 1] - qo_indptr_h[i];
+        const int64_t np = kv_p->indptr_h[i + 1] - kv_p->indptr_h[i];
+        const int64_t kvl = np > 0 ? (np - 1) * kv_p->page_size + kv_p->last_page_len_h[i] : 0;
+        for (int64_t r = 0; r < qo; ++r)  // keys row r sees
+          flops += (double)(causal ? std::max<int64_t>(0, std::min<int64_t>(kvl, r + 1 + kvl - qo)) : kvl);
+      }
+      flops *= 4.0 * hd * num_qo_heads;
+      const double bytes = (double)total_kv_d * kv_d->num_kv_heads * hd * eb * 2;
+      const double nd = cus * bytes * kPodPrefillCuRate / (flops * kPodDecodeWgRate + bytes * kPodPrefillCuRate);
+      slots = (int)std::lround(std::min<double>(2.0 * cus, std::max<double>(std::max(8, cus / 16), nd)));
+    }
     if (const char* env = std::getenv("FI_POD_DECODE_WG")) {
       const long n = std::strtol(env, nullptr, 10);
       if (n > 0 && n < (1 << 20)) slots = (int)n;
@@ -873,6 +898,10 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
     pp.n_decode_wg = (int32_t)nwg;
   }
   if (pp.n_prefill_wg + (int64_t)pp.n_decode_wg == 0) return FI_OK;
+  {
+    const char* env = std::getenv("FI_POD_ORDER");
+    pp.decode_first = (env && std::strcmp(env, "prefill_first") == 0) ? 0 : 1;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err = fi::launch_pod(pp, q_dtype, kv_p->k_dtype, o_dtype, hd, s);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill + decode kernel launch failed: %s", hipGetErrorString(err));

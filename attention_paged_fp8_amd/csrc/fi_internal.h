@@ -119,9 +119,10 @@ struct PrefillParamsT {
 };
 using PrefillParams = PrefillParamsT<kPrefillOrderMax>;
 
-// One launch over a prefill batch and a decode batch ("POD"): workgroups
-// [0, n_prefill_wg) run prefill work items in the heaviest-first order, the
-// next n_decode_wg run decode slices with kPodDecodeWaves waves each.  The
+// One launch over a prefill batch and a decode batch ("POD"): n_prefill_wg
+// workgroups run prefill work items in the heaviest-first order and
+// n_decode_wg run decode slices with kPodDecodeWaves waves each, the prefill
+// items first unless decode_first.  The
 // two plans share the kernel-argument budget of one launch, so their lists
 // are shorter than the separate calls'.
 constexpr int kPodDecodeWaves = 8;
@@ -132,6 +133,7 @@ struct PodParams {
   DecodeParamsT<kPodPrefixMax> dc;
   int32_t n_prefill_wg;
   int32_t n_decode_wg;
+  int32_t decode_first;  // 1: the decode slices take the first workgroup indices
 };
 static_assert(sizeof(PodParams) <= 4096, "POD kernel arguments exceed 4 KB");
 

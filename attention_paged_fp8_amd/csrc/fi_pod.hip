@@ -7,17 +7,21 @@
 // refuses fp8 KV there because its POD kernels instantiate the prefill
 // kernel's fragment traits, a limitation of that code and not of the method.
 //
-// Mapping onto gfx950.  A prefill workgroup (8 waves, 256 VGPRs each) fills
-// a CU's register file, so a decode workgroup cannot share a CU with one; a
-// single launch helps by keeping the GPU busy across the boundary between the
-// two batches: the hardware dispatches workgroups in index order, so the
-// prefill items (heaviest first) come first and the decode slices fill the
-// CUs as the prefill tail drains, with no gap between two kernels.  The
-// kernel runs 512 threads per workgroup: workgroup x < n_prefill_wg does the
-// prefill body's item x, the rest run the decode body with 8 waves, each wave
-// one (kv head, 16-row slice) as in the decode kernel, the workgroup reading
-// up to 8 heads' rows of each token.  Split decode rows are combined by the
-// decode merge kernel afterwards, as for fi_batch_decode_paged.
+// Mapping onto gfx950.  A prefill workgroup (8 waves, up to 256 VGPRs each)
+// fills a CU's register file, so a decode workgroup cannot share a CU with
+// one; the two phases share the GPU by CUs instead.  The decode stream is
+// bound by HBM, not by CUs: a few CUs stream it (each decode workgroup
+// reaching ~20 GB/s while the memory system is far from saturated) while the
+// other CUs compute prefill items, which then also take the CUs the decode
+// workgroups leave.  The hardware dispatches workgroups in index order, so
+// by default the decode slices come first, cut for a decode share of CUs that
+// balances the two phases' estimated durations, then the prefill items
+// (heaviest first); the prefill-first order remains selectable.  The kernel
+// runs 512 threads per workgroup: the decode workgroups run the decode body
+// with 8 waves, each wave one (kv head, 16-row slice) as in the decode
+// kernel, the workgroup reading up to 8 heads' rows of each token; the others
+// run the prefill body's items.  Split decode rows are combined by the decode
+// merge kernel afterwards, as for fi_batch_decode_paged.
 #include <type_traits>
 
 #include "fi_decode_body.hpp"
@@ -35,10 +39,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void pod_kernel(const PodPar
   constexpr int kLds = PC::LDS > DC::LDS ? PC::LDS : DC::LDS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   const int x = blockIdx.x;
-  if (x < p.n_prefill_wg)
-    prefill_body<QF, KVF, OBF16, D, false, false>(p.pf, x, 0, smem);
+  const int xp = p.decode_first ? x - p.n_decode_wg : x;  // prefill item, if >= 0
+  if (xp >= 0 && xp < p.n_prefill_wg)
+    prefill_body<QF, KVF, OBF16, D, false, false>(p.pf, xp, 0, smem);
   else
-    decode_body<QBF16, KVF, OBF16, D, 0, kPodDecodeWaves>(p.dc, x - p.n_prefill_wg, p.n_decode_wg, smem);
+    decode_body<QBF16, KVF, OBF16, D, 0, kPodDecodeWaves>(p.dc, p.decode_first ? x : x - p.n_prefill_wg,
+                                                          p.n_decode_wg, smem);
 }
 
 template <int QF, int KVF, bool OBF16, int D>

@@ -239,8 +239,13 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
  * in the order of fi_batch_prefill_paged for the prefill phase, then the same
  * for the decode phase (its sentences name "(decode phase)"), then the
  * cross-phase dtype and head checks, shapes and pointers, then workspace.
+ * The launch puts the decode slices first, on a share of the compute units
+ * sized so that both phases end together (a decode stream needs bandwidth
+ * more than CUs), and the prefill items on the rest.
  * Environment: FI_POD_DECODE_WG = a positive count of decode workgroups to
- * cut the decode phase into (default two per compute unit). */
+ * cut the decode phase into (default: that share; two per compute unit when
+ * the prefill phase is empty); FI_POD_ORDER = "prefill_first" dispatches the
+ * prefill items first. */
 fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const int32_t* qo_indptr_h, int32_t batch_p,
                              const fi_paged_kv* kv_p, int32_t causal, void* o_p, float* lse_p, const void* q_d,
                              int32_t batch_d, const fi_paged_kv* kv_d, void* o_d, float* lse_d, fi_dtype q_dtype,

@@ -94,6 +94,25 @@ def test_pod_small(gpu_device, case):
     assert np.array_equal(op, o2.double().cpu().numpy()) and np.array_equal(lp, l2.double().cpu().numpy())
 
 
+@pytest.mark.parametrize("order,wg", [("prefill_first", None), ("decode_first", "512"), ("decode_first", "16")])
+def test_pod_dispatch_orders(gpu_device, monkeypatch, order, wg):
+    """Both dispatch orders and decode shares far from the default give the
+    same results (the prefill phase bit for bit)."""
+    say("pod order", order, wg)
+    monkeypatch.setenv("FI_POD_ORDER", order)
+    if wg:
+        monkeypatch.setenv("FI_POD_DECODE_WG", wg)
+    wp = make_paged(77, qo_lens=[300, 17, 129], prefix_lens=[700, 0, 63], hq=32, hkv=8, d=128, page=16, q="f16",
+                    kvd="e4m3")
+    wd = make_paged(78, kv_lens=[1500, 33, 900, 0, 640], hq=32, hkv=8, d=128, page=16, q="f16", kvd="e4m3")
+    dp, dd = upload(wp, gpu_device), upload(wd, gpu_device)
+    (op, lp), (od, ld) = run_pod(wp, dp, wd, dd)
+    o_ref, l_ref = OA.batch_prefill(wp, causal=True)
+    assert_parity(op, lp, o_ref, l_ref, "f16", f"pod {order} {wg}, prefill")
+    o_ref, l_ref = OA.batch_decode(wd)
+    assert_parity(od, ld, o_ref, l_ref, "f16", f"pod {order} {wg}, decode")
+
+
 def test_pod_one_phase_empty(gpu_device):
     say("pod one phase empty")
     wp = make_paged(73, qo_lens=[90, 20], prefix_lens=[30, 0], hq=8, hkv=2, d=128, page=16, q="f16", kvd="e4m3")
