@@ -272,7 +272,7 @@ fi_status plan_decode(const char* fn, DP& p, int nw, int slots, fi_dtype q_dtype
       // that short streams run better at 2 per CU -- fewer, longer slices split
       // fewer requests and spread start-up over more bytes (measured: a slice
       // under ~640 KB of K/V loses at 3 per CU, one over ~850 KB gains).
-      slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim);
+      slots = fi::decode_slots(q_dtype, kv_dtype, o_dtype, head_dim, nw);
       const int cus = fi::device_cus();
       if (slots > 0 && cus > 0 && slots / cus > 2) {
         const int64_t row_bytes = (int64_t)(1 << hpw_shift) * head_dim * elem_bytes(kv_dtype) * 2;  // K + V per item
@@ -418,13 +418,37 @@ fi_status run_decode(const char* fn, fi::DecodeParams& p, fi_dtype q_dtype, fi_d
   if (use_scratch) workspace_bytes = fi::kDecodeScratchBytes;
   bool merge = false;
   size_t need = 0;
-  fi_status st = plan_decode(fn, p, fi::kDecodeWaves, 0, q_dtype, kv_dtype, o_dtype, batch, head_dim, indptr_h,
-                             last_page_len_h, page_size, max_kv, total_kv, have_ws, &merge, &need);
+  int nw = fi::kDecodeWaves;
+  fi_status st = plan_decode(fn, p, nw, 0, q_dtype, kv_dtype, o_dtype, batch, head_dim, indptr_h, last_page_len_h,
+                             page_size, max_kv, total_kv, have_ws, &merge, &need);
   if (st != FI_OK) return st;
+  // Long per-workgroup streams (a balanced slice of at least 1 MB of K/V) run
+  // on 8-wave workgroups that read whole rows of 8 heads: the long-context
+  // workload streams 4% faster that way, while short slices (the
+  // batch-decode workload's ~600 KB) gain nothing.
+  // FI_DECODE_WAVES = 4 or 8 forces the workgroup size (8 only where it exists).
+  const char* wv = std::getenv("FI_DECODE_WAVES");
+  const int force_nw = wv ? std::atoi(wv) : 0;
+  if (p.balanced && fi::decode_long_supported(q_dtype, kv_dtype) && force_nw != fi::kDecodeWaves) {
+    const int64_t row_bytes = (int64_t)(1 << p.hpw_shift) * head_dim * elem_bytes(kv_dtype) * 2;
+    if (force_nw == fi::kDecodeWavesLong || p.slice * row_bytes >= (1 << 20)) {
+      fi::DecodeParams p8 = p;
+      bool merge8 = false;
+      size_t need8 = 0;
+      if (plan_decode(fn, p8, fi::kDecodeWavesLong, 0, q_dtype, kv_dtype, o_dtype, batch, head_dim, indptr_h,
+                      last_page_len_h, page_size, max_kv, total_kv, have_ws, &merge8, &need8) == FI_OK &&
+          p8.balanced) {
+        p = p8;
+        merge = merge8;
+        need = need8;
+        nw = fi::kDecodeWavesLong;
+      }
+    }
+  }
   if ((st = decode_workspace(fn, need, &workspace, workspace_bytes, use_scratch, batch)) != FI_OK) return st;
   finish_decode(p, kv_dtype, batch, head_dim, sm_scale, k_scale, v_scale, workspace, need);
   if (batch == 0) return FI_OK;
-  hipError_t err = fi::launch_decode(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, stream);
+  hipError_t err = fi::launch_decode(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, nw, stream);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(err));
   if (merge) {
     err = launch_decode_merge(p, o_dtype, batch, head_dim, stream);

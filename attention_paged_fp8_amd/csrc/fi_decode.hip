@@ -50,15 +50,21 @@ namespace fi {
 #define FI_DECODE_MIN_WG_PER_CU 3
 #endif
 
-// Q8: an fp8 query (see decode_body).
-template <bool QBF16, int KVF, bool OBF16, int D, int Q8 = 0>
-// (the fnuz forms hold a step's codes in registers before widening them, and
-// are given the registers of two workgroups per CU)
-__global__ __launch_bounds__(256, (KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) ? 2 : FI_DECODE_MIN_WG_PER_CU) void
+// Q8: an fp8 query (see decode_body).  NW: waves per workgroup -- 4, or 8
+// for long per-workgroup streams, where a workgroup reading whole 1 KB rows
+// of 8 heads streams faster (long-context workload 287 -> 275 us).
+// The second launch bound is waves per SIMD: a 4-wave workgroup puts one wave
+// on each SIMD, an 8-wave one two.  The fnuz forms hold a step's codes in
+// registers before widening them, and get the registers of two workgroups per
+// CU; an 8-wave workgroup runs one per CU (its stage is twice as wide).
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8 = 0, int NW = kDecodeWaves>
+__global__ __launch_bounds__(64 * NW, (KVF == FMT_E4M3_FNUZ || KVF == FMT_E5M2_FNUZ) || NW == 8
+                                          ? 2
+                                          : FI_DECODE_MIN_WG_PER_CU) void
 decode_kernel(
     const DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeCfg<QBF16, KVF, OBF16, D, kDecodeWaves>::LDS];
-  decode_body<QBF16, KVF, OBF16, D, Q8, kDecodeWaves>(p, blockIdx.x, gridDim.x, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeCfg<QBF16, KVF, OBF16, D, NW>::LDS];
+  decode_body<QBF16, KVF, OBF16, D, Q8, NW>(p, blockIdx.x, gridDim.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -194,74 +200,93 @@ hipError_t decode_scratch(void** ptr) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <bool QBF16, int KVF, bool OBF16, int D, int Q8>
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8, int NW>
 static hipError_t launch_decode_t(const DecodeParams& p, int batch, hipStream_t s) {
   dim3 grid(p.balanced ? (unsigned)p.n_wg : (unsigned)p.max_chunks * p.n_hgroups * p.n_sgroups * batch);
   if (grid.x == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<QBF16, KVF, OBF16, D, Q8>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<QBF16, KVF, OBF16, D, Q8, NW>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
+// the 8-wave kernel where it exists (decode_long_supported), else the 4-wave one
+template <bool QBF16, int KVF, int Q8>
+constexpr bool kHasLong = Q8 == 0 && (KVF == FMT_E4M3 || KVF == FMT_E5M2 || KVF == (QBF16 ? FMT_BF16 : FMT_F16));
+
 template <bool QBF16, int KVF, bool OBF16, int Q8>
-static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, int batch, hipStream_t s) {
-  if (head_dim == 128) return launch_decode_t<QBF16, KVF, OBF16, 128, Q8>(p, batch, s);
-  return launch_decode_t<QBF16, KVF, OBF16, 64, Q8>(p, batch, s);
+static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, int batch, int nw, hipStream_t s) {
+  if constexpr (kHasLong<QBF16, KVF, Q8>) {
+    if (nw == kDecodeWavesLong) {
+      if (head_dim == 128) return launch_decode_t<QBF16, KVF, OBF16, 128, Q8, kDecodeWavesLong>(p, batch, s);
+      return launch_decode_t<QBF16, KVF, OBF16, 64, Q8, kDecodeWavesLong>(p, batch, s);
+    }
+  }
+  if (nw != kDecodeWaves) return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_decode_t<QBF16, KVF, OBF16, 128, Q8, kDecodeWaves>(p, batch, s);
+  return launch_decode_t<QBF16, KVF, OBF16, 64, Q8, kDecodeWaves>(p, batch, s);
 }
 
 template <bool QBF16, int KVF, int Q8>
-static hipError_t launch_decode_o(const DecodeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {
-  if (o_fmt == FMT_BF16) return launch_decode_d<QBF16, KVF, true, Q8>(p, head_dim, batch, s);
-  return launch_decode_d<QBF16, KVF, false, Q8>(p, head_dim, batch, s);
+static hipError_t launch_decode_o(const DecodeParams& p, int o_fmt, int head_dim, int batch, int nw, hipStream_t s) {
+  if (o_fmt == FMT_BF16) return launch_decode_d<QBF16, KVF, true, Q8>(p, head_dim, batch, nw, s);
+  return launch_decode_d<QBF16, KVF, false, Q8>(p, head_dim, batch, nw, s);
 }
 
 template <bool QBF16, int Q8>
-static hipError_t launch_decode_kv(const DecodeParams& p, int kv_fmt, int o_fmt, int head_dim, int batch,
+static hipError_t launch_decode_kv(const DecodeParams& p, int kv_fmt, int o_fmt, int head_dim, int batch, int nw,
                                    hipStream_t s) {
   switch (kv_fmt) {
-    case FMT_E4M3: return launch_decode_o<QBF16, FMT_E4M3, Q8>(p, o_fmt, head_dim, batch, s);
-    case FMT_E5M2: return launch_decode_o<QBF16, FMT_E5M2, Q8>(p, o_fmt, head_dim, batch, s);
-    case FMT_E4M3_FNUZ: return launch_decode_o<QBF16, FMT_E4M3_FNUZ, Q8>(p, o_fmt, head_dim, batch, s);
-    case FMT_E5M2_FNUZ: return launch_decode_o<QBF16, FMT_E5M2_FNUZ, Q8>(p, o_fmt, head_dim, batch, s);
+    case FMT_E4M3: return launch_decode_o<QBF16, FMT_E4M3, Q8>(p, o_fmt, head_dim, batch, nw, s);
+    case FMT_E5M2: return launch_decode_o<QBF16, FMT_E5M2, Q8>(p, o_fmt, head_dim, batch, nw, s);
+    case FMT_E4M3_FNUZ: return launch_decode_o<QBF16, FMT_E4M3_FNUZ, Q8>(p, o_fmt, head_dim, batch, nw, s);
+    case FMT_E5M2_FNUZ: return launch_decode_o<QBF16, FMT_E5M2_FNUZ, Q8>(p, o_fmt, head_dim, batch, nw, s);
   }
   if constexpr (Q8 != 0) {
     return hipErrorInvalidValue;  // an fp8 query needs an fp8 cache
   } else {
-    if (kv_fmt == FMT_F16) return launch_decode_o<QBF16, FMT_F16, 0>(p, o_fmt, head_dim, batch, s);
-    return launch_decode_o<QBF16, FMT_BF16, 0>(p, o_fmt, head_dim, batch, s);
+    if (kv_fmt == FMT_F16) return launch_decode_o<QBF16, FMT_F16, 0>(p, o_fmt, head_dim, batch, nw, s);
+    return launch_decode_o<QBF16, FMT_BF16, 0>(p, o_fmt, head_dim, batch, nw, s);
   }
 }
 
-template <bool QBF16, int KVF, bool OBF16, int D, int Q8>
+template <bool QBF16, int KVF, bool OBF16, int D, int Q8, int NW>
 static int occupancy_t() {
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&decode_kernel<QBF16, KVF, OBF16, D, Q8>),
-                                                   256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ,
+                                                   reinterpret_cast<const void*>(&decode_kernel<QBF16, KVF, OBF16, D, Q8, NW>),
+                                                   64 * NW, 0) != hipSuccess)
     return 0;
   return occ;
 }
 
 template <bool QBF16, int KVF, bool OBF16, int Q8>
-static int occupancy_d(int d) {
-  return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128, Q8>() : occupancy_t<QBF16, KVF, OBF16, 64, Q8>();
+static int occupancy_d(int d, int nw) {
+  if constexpr (kHasLong<QBF16, KVF, Q8>) {
+    if (nw == kDecodeWavesLong)
+      return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128, Q8, kDecodeWavesLong>()
+                      : occupancy_t<QBF16, KVF, OBF16, 64, Q8, kDecodeWavesLong>();
+  }
+  if (nw != kDecodeWaves) return 0;
+  return d == 128 ? occupancy_t<QBF16, KVF, OBF16, 128, Q8, kDecodeWaves>()
+                  : occupancy_t<QBF16, KVF, OBF16, 64, Q8, kDecodeWaves>();
 }
 
 template <bool QBF16, int KVF, int Q8>
-static int occupancy_o(int o, int d) {
-  return o == FMT_BF16 ? occupancy_d<QBF16, KVF, true, Q8>(d) : occupancy_d<QBF16, KVF, false, Q8>(d);
+static int occupancy_o(int o, int d, int nw) {
+  return o == FMT_BF16 ? occupancy_d<QBF16, KVF, true, Q8>(d, nw) : occupancy_d<QBF16, KVF, false, Q8>(d, nw);
 }
 
 template <bool QBF16, int Q8>
-static int occupancy_kv(int kv, int o, int d) {
+static int occupancy_kv(int kv, int o, int d, int nw) {
   switch (kv) {
-    case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3, Q8>(o, d);
-    case FMT_E5M2: return occupancy_o<QBF16, FMT_E5M2, Q8>(o, d);
-    case FMT_E4M3_FNUZ: return occupancy_o<QBF16, FMT_E4M3_FNUZ, Q8>(o, d);
-    case FMT_E5M2_FNUZ: return occupancy_o<QBF16, FMT_E5M2_FNUZ, Q8>(o, d);
+    case FMT_E4M3: return occupancy_o<QBF16, FMT_E4M3, Q8>(o, d, nw);
+    case FMT_E5M2: return occupancy_o<QBF16, FMT_E5M2, Q8>(o, d, nw);
+    case FMT_E4M3_FNUZ: return occupancy_o<QBF16, FMT_E4M3_FNUZ, Q8>(o, d, nw);
+    case FMT_E5M2_FNUZ: return occupancy_o<QBF16, FMT_E5M2_FNUZ, Q8>(o, d, nw);
   }
   if constexpr (Q8 != 0) {
     return 0;
   } else {
-    return kv == FMT_F16 ? occupancy_o<QBF16, FMT_F16, 0>(o, d) : occupancy_o<QBF16, FMT_BF16, 0>(o, d);
+    return kv == FMT_F16 ? occupancy_o<QBF16, FMT_F16, 0>(o, d, nw) : occupancy_o<QBF16, FMT_BF16, 0>(o, d, nw);
   }
 }
 
@@ -276,32 +301,32 @@ int device_cus() {
   return v;
 }
 
-int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim) {
+int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim, int nw) {
   // cached per (device, instantiation): the values cannot change while the process runs
-  static std::atomic<int> cache[64][4][10][2][2];
+  static std::atomic<int> cache[64][4][10][2][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || kv_fmt < 0 || kv_fmt >= 10) return 0;
   const int qi = q_fmt == FMT_BF16 ? 1 : q_fmt == FMT_E4M3 ? 2 : q_fmt == FMT_E5M2 ? 3 : 0;
-  std::atomic<int>& slot = cache[dev][qi][kv_fmt][o_fmt == FMT_BF16][head_dim == 128];
+  std::atomic<int>& slot = cache[dev][qi][kv_fmt][o_fmt == FMT_BF16][head_dim == 128][nw == kDecodeWavesLong];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int occ = qi == 1   ? occupancy_kv<true, 0>(kv_fmt, o_fmt, head_dim)
-                  : qi == 2 ? occupancy_kv<false, FMT_E4M3>(kv_fmt, o_fmt, head_dim)
-                  : qi == 3 ? occupancy_kv<false, FMT_E5M2>(kv_fmt, o_fmt, head_dim)
-                            : occupancy_kv<false, 0>(kv_fmt, o_fmt, head_dim);
+  const int occ = qi == 1   ? occupancy_kv<true, 0>(kv_fmt, o_fmt, head_dim, nw)
+                  : qi == 2 ? occupancy_kv<false, FMT_E4M3>(kv_fmt, o_fmt, head_dim, nw)
+                  : qi == 3 ? occupancy_kv<false, FMT_E5M2>(kv_fmt, o_fmt, head_dim, nw)
+                            : occupancy_kv<false, 0>(kv_fmt, o_fmt, head_dim, nw);
   v = cus * occ;
   slot.store(v, std::memory_order_relaxed);
   return v;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
+hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch, int nw,
                          hipStream_t s) {
-  if (q_fmt == FMT_BF16) return launch_decode_kv<true, 0>(p, kv_fmt, o_fmt, head_dim, batch, s);
-  if (q_fmt == FMT_E4M3) return launch_decode_kv<false, FMT_E4M3>(p, kv_fmt, o_fmt, head_dim, batch, s);
-  if (q_fmt == FMT_E5M2) return launch_decode_kv<false, FMT_E5M2>(p, kv_fmt, o_fmt, head_dim, batch, s);
-  return launch_decode_kv<false, 0>(p, kv_fmt, o_fmt, head_dim, batch, s);
+  if (q_fmt == FMT_BF16) return launch_decode_kv<true, 0>(p, kv_fmt, o_fmt, head_dim, batch, nw, s);
+  if (q_fmt == FMT_E4M3) return launch_decode_kv<false, FMT_E4M3>(p, kv_fmt, o_fmt, head_dim, batch, nw, s);
+  if (q_fmt == FMT_E5M2) return launch_decode_kv<false, FMT_E5M2>(p, kv_fmt, o_fmt, head_dim, batch, nw, s);
+  return launch_decode_kv<false, 0>(p, kv_fmt, o_fmt, head_dim, batch, nw, s);
 }
 
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s) {

@@ -11,6 +11,7 @@ namespace fi {
 enum Fmt : int { FMT_F16 = 1, FMT_BF16 = 2, FMT_E4M3 = 3, FMT_E5M2 = 4, FMT_E4M3_FNUZ = 8, FMT_E5M2_FNUZ = 9 };
 
 constexpr int kDecodeWaves = 4;         // waves per decode workgroup, one (kv head, row slice) each
+constexpr int kDecodeWavesLong = 8;     // the same for long per-workgroup streams (whole 1 KB rows of 8 heads)
 constexpr int kDecodeStep = 16;         // tokens staged per step
 constexpr int kChunkQuantum = 64;       // split-KV chunk granularity (tokens)
 constexpr int kDecodeRows = 16;         // q rows per decode MFMA tile (one GQA slice)
@@ -139,11 +140,17 @@ static_assert(sizeof(PodParams) <= 4096, "POD kernel arguments exceed 4 KB");
 
 // Kernel launchers (defined in the .hip translation units).  They return the
 // hipError_t of the launch.
-hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,
+// nw: kDecodeWaves, or kDecodeWavesLong where decode_long_supported().
+hipError_t launch_decode(const DecodeParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch, int nw,
                          hipStream_t s);
+// The 8-wave decode kernel exists for a 2-byte query over an OCP fp8 cache or
+// a cache of the query's own type.
+inline bool decode_long_supported(int q_fmt, int kv_fmt) {
+  return (q_fmt == FMT_F16 || q_fmt == FMT_BF16) && (kv_fmt == FMT_E4M3 || kv_fmt == FMT_E5M2 || kv_fmt == q_fmt);
+}
 hipError_t launch_merge(const MergeParams& p, int o_fmt, int head_dim, int batch, hipStream_t s);
 // Workgroups of the decode kernel for these types that fit on the current device at once.
-int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim);
+int decode_slots(int q_fmt, int kv_fmt, int o_fmt, int head_dim, int nw = kDecodeWaves);
 int device_cus();  // compute units of the current device (0 on error), cached
 // ragged: K/V rows addressed as indptr[b] + t (stride st) instead of a page table
 hipError_t launch_prefill(const PrefillParams& p, int q_fmt, int kv_fmt, int o_fmt, int head_dim, int batch,

@@ -160,7 +160,10 @@ size_t fi_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t he
  *            longest kv_len).
  * Environment: FI_SPLIT_KV = "off" disables splitting, a positive integer
  * forces that many tokens per chunk (rounded up to a multiple of 64), unset
- * or "auto" lets the planner choose (fixed_split_size). */
+ * or "auto" lets the planner choose (fixed_split_size).  FI_DECODE_WAVES = 4
+ * or 8 forces the decode workgroup size (8: for a 2-byte query over an OCP
+ * fp8 cache or one of its own type, under the planner's balanced split);
+ * unset, 8 is used where a workgroup's slice holds at least 1 MB of K/V. */
 fi_status fi_batch_decode_paged(const void* q, fi_dtype q_dtype, int32_t batch, int32_t num_qo_heads,
                                 const fi_paged_kv* kv, void* o, fi_dtype o_dtype, float* lse, float sm_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);

@@ -111,6 +111,39 @@ def test_decode_small(gpu_device, case):
             assert np.all(og[i] == 0) and np.all(np.isneginf(lg[i]))
 
 
+# ------------------------------------------------------------------ 8-wave workgroups
+LONG = [
+    # (kvd, q, o, page, d, hq, hkv, lens)
+    ("e4m3", "bf16", "bf16", 16, 128, 32, 8, (1, 31, 700, 2049, 0, 517)),
+    ("e5m2", "f16", "f16", 64, 128, 64, 8, (1000, 3, 4097)),
+    ("e4m3", "f16", "bf16", 4, 64, 8, 2, (77, 300, 1, 900)),
+    ("e5m2", "bf16", "f16", 1, 64, 4, 4, (9, 40, 130)),
+    ("e4m3", "f16", "f16", 128, 128, 32, 1, (1500, 260)),   # group 32: two 16-row slices
+    ("e4m3", "f16", "f16", 32, 128, 12, 4, (100, 333)),     # group 3
+    ("f16", "f16", "f16", 16, 128, 32, 8, (400, 65, 1)),
+    ("bf16", "bf16", "bf16", 16, 64, 16, 2, (257, 31)),
+    ("e4m3", "bf16", "bf16", 16, 128, 16, 16, (55, 1, 0, 1024)),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[f"{c[0]}-q{c[1]}-o{c[2]}-p{c[3]}-d{c[4]}-h{c[5]}x{c[6]}" for c in LONG])
+def test_decode_eight_wave_workgroups(gpu_device, monkeypatch, case):
+    """The 8-wave decode kernel (whole rows of up to 8 kv heads per
+    workgroup), which the planner picks for long per-workgroup streams,
+    forced on small shapes: parity with the oracle."""
+    kvd, q, o, page, d, hq, hkv, lens = case
+    say("decode 8 waves", case)
+    monkeypatch.setenv("FI_DECODE_WAVES", "8")
+    w = make_paged(13, kv_lens=list(lens), hq=hq, hkv=hkv, d=d, page=page, q=q, kvd=kvd, o=o, extra_pages=3)
+    dv = upload(w, gpu_device)
+    o_ref, l_ref = OA.batch_decode(w)
+    og, lg, _ = run_decode(w, dv)
+    assert_parity(og, lg, o_ref, l_ref, o, str(case))
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert np.all(og[i] == 0) and np.all(np.isneginf(lg[i]))
+
+
 # ------------------------------------------------------------------ full-size workloads
 @pytest.mark.parametrize("wl", ["batch_decode", "long_context_decode"])
 def test_workload_full_size(gpu_device, wl):
