@@ -509,11 +509,13 @@ fi_status check_queries(const char* fn, const void* q, void* o, int32_t batch, c
 
 // Work-group shape, scales and dispatch order of a prefill batch; p already
 // holds the tensors and the K/V addressing.
+// kv_base_h: the host copy of the cache's indptr (a request's first page, or
+// first row of a ragged cache), or NULL for a single request (row 0).
 template <class PP>
 fi_status plan_prefill(const char* fn, PP& p, fi_dtype kv_dtype, int32_t batch, int32_t num_qo_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t causal, int64_t max_qo,
                        const int32_t* qo_indptr_h, const std::vector<int64_t>& kv_len, float sm_scale, float k_scale,
-                       float v_scale) {
+                       float v_scale, const int32_t* kv_base_h) {
   p.num_qo_heads = num_qo_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_qo_heads / num_kv_heads;
@@ -532,6 +534,16 @@ fi_status plan_prefill(const char* fn, PP& p, fi_dtype kv_dtype, int32_t batch, 
   if (p.n_qblocks > 65535) return fail(FI_E_SHAPE, fn, "longest request has %lld queries; at most %d are supported",
                                        (long long)max_qo, 65535 * p.q_per_wg);
   plan_prefill_order(p, batch, qo_indptr_h, kv_len);
+  p.n_geo = 0;
+  if (batch <= PP::kGeoMax) {
+    for (int32_t i = 0; i < batch; ++i) {
+      p.geo[i][0] = qo_indptr_h[i];
+      p.geo[i][1] = qo_indptr_h[i + 1] - qo_indptr_h[i];
+      p.geo[i][2] = kv_base_h ? kv_base_h[i] : 0;
+      p.geo[i][3] = (int32_t)kv_len[i];
+    }
+    p.n_geo = batch;
+  }
   return FI_OK;
 }
 
@@ -540,9 +552,9 @@ fi_status run_prefill(const char* fn, fi::PrefillParams& p, fi_dtype q_dtype, fi
                              fi_dtype o_dtype, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t causal, int64_t max_qo, const int32_t* qo_indptr_h,
                              const std::vector<int64_t>& kv_len, float sm_scale, float k_scale, float v_scale,
-                             bool ragged, hipStream_t stream) {
+                             bool ragged, hipStream_t stream, const int32_t* kv_base_h) {
   fi_status st = plan_prefill(fn, p, kv_dtype, batch, num_qo_heads, num_kv_heads, head_dim, causal, max_qo,
-                              qo_indptr_h, kv_len, sm_scale, k_scale, v_scale);
+                              qo_indptr_h, kv_len, sm_scale, k_scale, v_scale, kv_base_h);
   if (st != FI_OK) return st;
   hipError_t err = fi::launch_prefill(p, q_dtype, kv_dtype, o_dtype, head_dim, batch, ragged, stream);
   if (err != hipSuccess) return fail(FI_E_HIP, fn, "prefill kernel launch failed: %s", hipGetErrorString(err));
@@ -737,7 +749,7 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
   p.page_size = kv->page_size;
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale, kv->v_scale, false,
-                     reinterpret_cast<hipStream_t>(stream));
+                     reinterpret_cast<hipStream_t>(stream), kv->indptr_h);
 }
 
 fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_scale, const int32_t* qo_indptr,
@@ -782,7 +794,7 @@ fi_status fi_batch_prefill_paged_fp8q(const void* q, fi_dtype q_dtype, float q_s
   // q_scale joins k_scale in the logit scale (both multiply the fp32 products)
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * q_scale, kv->v_scale, false,
-                     reinterpret_cast<hipStream_t>(stream));
+                     reinterpret_cast<hipStream_t>(stream), kv->indptr_h);
 }
 
 // Prefill and decode batches in one launch.  Both phases must agree on the
@@ -830,7 +842,7 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
   fi::PodParams pp{};
   // prefill phase: every (request, query block) pair in the dispatch order
   if (batch_p > 0 && max_qo > 0) {
-    fi::PrefillParamsT<fi::kPodOrderMax>& f = pp.pf;
+    auto& f = pp.pf;
     f.q = q_p;
     f.o = o_p;
     f.lse = lse_p;
@@ -851,7 +863,7 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
       kv_len[i] = np > 0 ? (np - 1) * kv_p->page_size + kv_p->last_page_len_h[i] : 0;
     }
     if ((st = plan_prefill(fn, f, kv_p->k_dtype, batch_p, num_qo_heads, kv_p->num_kv_heads, hd, causal, max_qo,
-                           qo_indptr_h, kv_len, sm_scale, kv_p->k_scale, kv_p->v_scale)) != FI_OK)
+                           qo_indptr_h, kv_len, sm_scale, kv_p->k_scale, kv_p->v_scale, kv_p->indptr_h)) != FI_OK)
       return st;
     if (f.n_items == 0)
       return fail(FI_E_SHAPE, fn, "the prefill phase has more than %d (request, query block) pairs of %d queries, the "
@@ -988,7 +1000,7 @@ static fi_status ragged_prefill(const char* fn, bool q8, const void* q, fi_dtype
   p.pv_fp8 = (q8 && pv_fp8) ? 1 : 0;
   return run_prefill(fn, p, q_dtype, kv->k_dtype, o_dtype, batch, num_qo_heads, kv->num_kv_heads, kv->head_dim,
                      causal, max_qo, qo_indptr_h, kv_len, sm_scale, kv->k_scale * (q8 ? q_scale : 1.0f), kv->v_scale,
-                     true, reinterpret_cast<hipStream_t>(stream));
+                     true, reinterpret_cast<hipStream_t>(stream), kv->indptr_h);
 }
 
 static fi_status single_prefill(const char* fn, bool q8, const void* q, fi_dtype q_dtype, float q_scale,
@@ -1028,7 +1040,7 @@ static fi_status single_prefill(const char* fn, bool q8, const void* q, fi_dtype
   const std::vector<int64_t> lens(1, kv_len);
   return run_prefill(fn, p, q_dtype, k_dtype, o_dtype, 1, num_qo_heads, num_kv_heads, head_dim, causal, qo_len,
                      qo_indptr_h, lens, sm_scale, k_scale * (q8 ? q_scale : 1.0f), v_scale, true,
-                     reinterpret_cast<hipStream_t>(stream));
+                     reinterpret_cast<hipStream_t>(stream), nullptr);
 }
 
 extern "C" {

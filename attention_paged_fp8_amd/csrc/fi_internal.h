@@ -81,13 +81,17 @@ struct MergeParams {
 // Prefill workgroups: waves of 32 query rows sharing each K/V tile.
 constexpr int kPrefillWaves = 8;
 // Largest number of (request, query block) pairs whose dispatch order travels
-// in the kernel arguments (4 bytes each).
-constexpr int kPrefillOrderMax = 768;
+// in the kernel arguments (4 bytes each), and of requests whose geometry does
+// (16 bytes each).
+constexpr int kPrefillOrderMax = 512;
+constexpr int kPrefillGeoMax = 96;
 
-// NORD: capacity of the dispatch order carried in the arguments
-template <int NORD>
+// NORD: capacity of the dispatch order carried in the arguments; NGEO: of
+// the request geometry
+template <int NORD, int NGEO>
 struct PrefillParamsT {
   static constexpr int kOrderMax = NORD;
+  static constexpr int kGeoMax = NGEO;
   const void* q;          // [total_q, Hqo, D]
   void* o;
   float* lse;
@@ -117,8 +121,14 @@ struct PrefillParamsT {
   // first; otherwise x = (request, kv head, head group) and y = query block.
   int32_t n_items;
   uint32_t order[NORD];
+  // Request geometry from the host's copies of the index arrays, so that a
+  // workgroup's first page-id loads need no device load before them: per
+  // request, its first query row, queries, first page (ragged: first K/V row)
+  // and keys.  n_geo = batch when it fits, else 0 (read from the device).
+  int32_t n_geo;
+  int32_t geo[NGEO][4];
 };
-using PrefillParams = PrefillParamsT<kPrefillOrderMax>;
+using PrefillParams = PrefillParamsT<kPrefillOrderMax, kPrefillGeoMax>;
 
 // One launch over a prefill batch and a decode batch ("POD"): n_prefill_wg
 // workgroups run prefill work items in the heaviest-first order and
@@ -127,16 +137,19 @@ using PrefillParams = PrefillParamsT<kPrefillOrderMax>;
 // two plans share the kernel-argument budget of one launch, so their lists
 // are shorter than the separate calls'.
 constexpr int kPodDecodeWaves = 8;
-constexpr int kPodOrderMax = 448;
-constexpr int kPodPrefixMax = 320;
+constexpr int kPodOrderMax = 384;
+constexpr int kPodGeoMax = 48;
+constexpr int kPodPrefixMax = 256;
 struct PodParams {
-  PrefillParamsT<kPodOrderMax> pf;
+  PrefillParamsT<kPodOrderMax, kPodGeoMax> pf;
   DecodeParamsT<kPodPrefixMax> dc;
   int32_t n_prefill_wg;
   int32_t n_decode_wg;
   int32_t decode_first;  // 1: the decode slices take the first workgroup indices
 };
 static_assert(sizeof(PodParams) <= 4096, "POD kernel arguments exceed 4 KB");
+static_assert(sizeof(PrefillParams) <= 4096, "prefill kernel arguments exceed 4 KB");
+static_assert(sizeof(DecodeParams) <= 4096, "decode kernel arguments exceed 4 KB");
 
 // Kernel launchers (defined in the .hip translation units).  They return the
 // hipError_t of the launch.

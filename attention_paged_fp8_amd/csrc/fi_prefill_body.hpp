@@ -144,18 +144,27 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
   // request geometry: uniform over the workgroup, kept in scalar registers so
   // that the tile loop and its branches stay scalar
   // (a single request passes its lengths in the arguments instead of indptrs)
-  const int q_begin = p.qo_indptr ? uniform(p.qo_indptr[b]) : 0;
-  const int qo_len = p.qo_indptr ? uniform(p.qo_indptr[b + 1]) - q_begin : p.single_qo_len;
+  // (from the kernel arguments when the host passed them: the first page-id
+  // loads then wait for no device load)
+  int q_begin, qo_len, a, kv_len;
+  if (b < p.n_geo) {
+    q_begin = p.geo[b][0];
+    qo_len = p.geo[b][1];
+    a = p.geo[b][2];
+    kv_len = p.geo[b][3];
+  } else {
+    q_begin = p.qo_indptr ? uniform(p.qo_indptr[b]) : 0;
+    qo_len = p.qo_indptr ? uniform(p.qo_indptr[b + 1]) - q_begin : p.single_qo_len;
+    a = p.indptr ? uniform(p.indptr[b]) : 0;
+    if (RAGGED) {
+      kv_len = p.indptr ? uniform(p.indptr[b + 1]) - a : p.single_kv_len;
+    } else {
+      const int e = uniform(p.indptr[b + 1]);
+      kv_len = (e > a) ? (e - a - 1) * p.page_size + uniform(p.last_page_len[b]) : 0;
+    }
+  }
   const int q0 = qb * p.q_per_wg;
   if (q0 >= qo_len) return;
-  const int a = p.indptr ? uniform(p.indptr[b]) : 0;
-  int kv_len;
-  if (RAGGED) {
-    kv_len = p.indptr ? uniform(p.indptr[b + 1]) - a : p.single_kv_len;
-  } else {
-    const int e = uniform(p.indptr[b + 1]);
-    kv_len = (e > a) ? (e - a - 1) * p.page_size + uniform(p.last_page_len[b]) : 0;
-  }
   const int prefix = kv_len - qo_len;
 
   const int tid = threadIdx.x;

@@ -237,7 +237,7 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
  * Results are those of the two separate calls (the prefill phase bit for bit;
  * the decode phase within tolerance: it is cut into slices for 8-wave
  * workgroups instead of the decode kernel's 4).  The prefill phase may hold at
- * most 448 (request, block of 256 / heads_per_group query rows) pairs, which
+ * most 384 (request, block of 256 / heads_per_group query rows) pairs, which
  * the launch's arguments carry; more is refused with FI_E_SHAPE.  Checks run
  * in the order of fi_batch_prefill_paged for the prefill phase, then the same
  * for the decode phase (its sentences name "(decode phase)"), then the

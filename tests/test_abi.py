@@ -494,8 +494,8 @@ def test_pod_refusals(L):
     lens = np.full(449, 40)
     kvp, keepp = _kv(ptrs=True, lens=lens)
     qo = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    assert _pod(L, kvp, kv, batch_p=449, ptrs=True, qo=qo) == 2 and "at most 448" not in _err(L)
-    assert "more than 448 (request, query block) pairs" in _err(L), _err(L)
+    assert _pod(L, kvp, kv, batch_p=449, ptrs=True, qo=qo) == 2
+    assert "more than 384 (request, query block) pairs" in _err(L), _err(L)
 
 
 @no_gpu

@@ -231,7 +231,7 @@ def test_prefill_requests_without_queries_or_keys(gpu_device, causal):
 
 def test_prefill_many_query_blocks(gpu_device):
     """More (request, query block) pairs than the dispatch order carried in the
-    kernel arguments holds (768): the kernel then walks the grid in request
+    kernel arguments holds (512): the kernel then walks the grid in request
     order.  800 short requests, one query block each, against the oracle."""
     say("prefill 800 requests")
     rng = np.random.default_rng(800)
