@@ -28,7 +28,8 @@ What is computed, and where the pages state it:
       - lse is the natural-log log-sum-exp of the scaled logits;
       - a row with no visible key has o = 0 and lse = -inf (the identity of the
         state merge); a NaN stored in K or V is not an empty row, it
-        propagates through the arithmetic as IEEE floats do.
+        propagates through the arithmetic as IEEE floats do, to the rows
+        that see its key and to no other.
   * The split-KV state merge (PR #2148, the fixed_split_size /
     disable_split_kv plan arguments): L = ln sum_c exp(lse_c),
     o = sum_c exp(lse_c - L) o_c.
@@ -134,7 +135,15 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool, sm_s
         p = np.exp(s - m_safe)  # exp(-inf) = 0 on masked entries
         denom = p.sum(axis=-1, keepdims=True)
         w = np.where(has, p / np.where(has, denom, 1.0), 0.0)
-        og = (w.reshape(n_q * group, n_kv) @ vg).reshape(n_q, group, d)
+        # a key the mask hides contributes nothing to a row, also when its
+        # stored V is not finite (a zero weight times NaN or inf would reach
+        # the row): the product runs over finite V, and each non-finite
+        # element is added to the rows that see its key alone
+        vfin = np.isfinite(vg)
+        og = (w.reshape(n_q * group, n_kv) @ np.where(vfin, vg, 0.0)).reshape(n_q, group, d)
+        for t, c in zip(*np.nonzero(~vfin)):
+            sees = allowed[:, t]
+            og[sees, :, c] += w[sees, :, t] * vg[t, c]
         o[:, g * group:(g + 1) * group, :] = og
         lse[:, g * group:(g + 1) * group] = np.where(has[..., 0], m[..., 0] + np.log(np.where(has[..., 0], denom[..., 0], 1.0)), -np.inf)
     return o, lse

@@ -18,8 +18,10 @@ Pins, and what fixes them independently of the oracle's own code:
     Test plan, k_scale/v_scale item); the same for q_scale of an fp8 query;
   * causal: with no prefix, query row 0 sees only key 0 and the last row sees
     every key;
-  * a NaN stored in K poisons exactly the rows that read it (brute force), and
-    the contiguous single-decode form equals the scalar loops.
+  * a NaN stored in K poisons exactly the rows that read it, and a NaN or inf
+    stored in V only the rows that see its key, in its own column (brute
+    force, which skips hidden keys); the contiguous single-decode form equals
+    the scalar loops.
 """
 import importlib.util
 import math
@@ -296,6 +298,30 @@ def pin_nan_propagates(M):
     np.testing.assert_allclose(om[0], [3.0, 4.0], atol=1e-15)
 
 
+def pin_masked_nonfinite_v(M):
+    """A NaN and an inf stored in V under a causal mask reach, in their own
+    column, exactly the rows that see their key (brute force skips hidden
+    keys): rows the mask hides the key from stay finite, and so does every
+    LSE."""
+    w = _tiny_prefill(5, kvd="e5m2", qo=(1, 3, 5), prefix=(0, 2, 6))
+    i, ps = 2, w["page_size"]
+    n_kv = 11  # 5 queries after a prefix of 6: row r sees keys t <= r + 6
+    assert A.kv_len_of(w["indptr"], w["last_page_len"], ps, i) == n_kv
+    for t, g, c, code in ((8, 1, 3, 0x7F), (9, 0, 5, 0x7C)):  # e5m2 NaN, +inf
+        w["v_pool"][w["indices"][w["indptr"][i] + t // ps], t % ps, g, c] = code
+    o, l = M.batch_prefill(w, causal=True)
+    ob, lb = brute_force(w, causal=True)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+    a = int(w["qo_indptr"][i])
+    assert np.isfinite(l).all()
+    assert np.isfinite(o[a:a + 2, 2:4, 3]).all() and np.isnan(o[a + 2:a + 5, 2:4, 3]).all()
+    assert np.isfinite(o[a:a + 3, 0:2, 5]).all() and np.isposinf(o[a + 3:a + 5, 0:2, 5]).all()
+    o[a + 2:a + 5, 2:4, 3] = 0.0
+    o[a + 3:a + 5, 0:2, 5] = 0.0
+    assert np.isfinite(o).all()
+
+
 def pin_single_decode(M):
     """single_decode on contiguous K/V rows against the scalar-loop definition
     of a one-request paged workload holding the same rows (pages contiguous)."""
@@ -310,7 +336,7 @@ def pin_single_decode(M):
         np.testing.assert_allclose(l, lb[0], rtol=0, atol=1e-12)
 
 
-PINS = [pin_empty_request, pin_nan_propagates, pin_single_decode, pin_brute_force_decode, pin_brute_force_prefill, pin_closed_forms, pin_weights_sum_to_one,
+PINS = [pin_empty_request, pin_nan_propagates, pin_masked_nonfinite_v, pin_single_decode, pin_brute_force_decode, pin_brute_force_prefill, pin_closed_forms, pin_weights_sum_to_one,
         pin_page_permutation, pin_decode_equals_prefill_one_query, pin_split_merge,
         pin_gqa_equals_repeated_mha, pin_kscale_fold, pin_fp8_query, pin_causal_rows, pin_sampled_rows]
 
@@ -333,7 +359,8 @@ MUTATIONS = {
     "last_page_off_by_one": ("return (npages - 1) * page_size + int(last_page_len[i])", "return (npages - 1) * page_size + int(last_page_len[i]) - 1"),
     "slot_uses_page_index": ("slots = t % page_size", "slots = (t // page_size) % page_size"),
     "merge_unweighted": ("o = (coef[..., None] * o_parts).sum(axis=0)", "o = o_parts.mean(axis=0)"),
-    "transposed_pv": ("og = (w.reshape(n_q * group, n_kv) @ vg)", "og = (w.reshape(n_q * group, n_kv) @ vg[::-1])"),
+    "transposed_pv": ("@ np.where(vfin, vg, 0.0))", "@ np.where(vfin, vg, 0.0)[::-1])"),
+    "masked_v_leaks": ("@ np.where(vfin, vg, 0.0))", "@ vg)"),
     "default_scale_wrong": ("return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
     "nan_as_empty_row": ("has = np.broadcast_to(allowed.any(axis=-1)[:, None, None], m.shape)", "has = np.isfinite(m)"),
     "single_v_scale_dropped": ("v = decode_elements(v_raw, kv_dtype) * float(v_scale)", "v = decode_elements(v_raw, kv_dtype)"),
