@@ -38,13 +38,14 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-# Per-source flags.  The prefill kernel zeroes every out-of-range or poisoned
-# element before it reaches arithmetic, so it produces no NaN; without IEEE-mode
-# NaN quieting its max reductions take one instruction per element instead of
-# three.  (The decode kernel gains nothing from this and spills with it.)
 # Host-only sanitizer flags of the --sanitize build (applied to fi_api.cpp and the link).
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 SANITIZE_LIB = os.path.join(HERE, "_sanitize", "libfi.so")
+# Per-source flags.  The prefill kernel zeroes every out-of-range or poisoned
+# element before it reaches arithmetic, so it produces no NaN; without IEEE-mode
+# NaN quieting its max reductions take one instruction per element instead of
+# three.  (The decode kernel gains nothing from this and spills with it.)  The
+# fused kernel runs the prefill body, and its decode body tolerates the flags.
 PER_SOURCE = {"fi_prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
               "fi_pod.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 

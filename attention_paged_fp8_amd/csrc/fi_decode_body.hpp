@@ -359,8 +359,8 @@ __device__ __forceinline__ void decode_body(const P& p, const int bid, const int
     if (!row_ok) return;
     // a row without keys has sums of exactly 0; a NaN read from the cache
     // makes them NaN, which then carries into o and lse
-    const float inv = (lr_run != 0.f) ? 1.f / lr_run : 0.f;
-    const float lse2 = (l_run != 0.f) ? m_run + fast_log2(l_run) : kNegInf;
+    const float inv = has_weight(lr_run) ? 1.f / lr_run : 0.f;
+    const float lse2 = has_weight(l_run) ? m_run + fast_log2(l_run) : kNegInf;
     if (nchunks == 1) {
       const float f = inv * p.v_scale;
       uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)b * p.num_qo_heads + h) * D + 4 * qg;

@@ -297,6 +297,16 @@ __device__ __forceinline__ f32x16_t mfma32x32x64_f8(uint4 a0, uint4 a1, uint4 b0
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+// A row's sum of probabilities is +0 (no visible key), positive, or NaN (a
+// NaN read from the cache).  The test reads the bits through an empty asm
+// statement: in code compiled with NaNs assumed absent the compiler would
+// otherwise fold a test of the bits (it can prove the sum is never -0) into
+// an ordered float compare, which takes NaN for +0.
+__device__ __forceinline__ bool has_weight(float l) {
+  uint32_t b = __float_as_uint(l);
+  asm volatile("" : "+v"(b));
+  return b != 0u;
+}
 
 // Round an fp32 to q's 2-byte type and return (bits, value as fp32).
 template <bool BF16>

@@ -583,7 +583,9 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
   l_run = Cfg::kF32Lse ? sum_half_swap(l_run) : lr_run;
   if (!row_ok) return;
   const float lnorm = P8 ? l_run : lr_run;  // fp8 probabilities: the fp32 sum
-  const float inv = (lnorm > 0.f) ? p.v_scale / lnorm : 0.f;
+  // a row without visible keys has sums of exactly +0; a NaN read from the
+  // cache makes them NaN, which then carries into o and lse
+  const float inv = has_weight(lnorm) ? p.v_scale / lnorm : 0.f;
   uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(q_begin + qpos) * p.num_qo_heads + hq) * D;
 #pragma unroll
   for (int db = 0; db < Cfg::NDB; ++db)
@@ -596,7 +598,7 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
     }
   if (p.lse && hh == 0)
     p.lse[(int64_t)(q_begin + qpos) * p.num_qo_heads + hq] =
-        (l_run > 0.f) ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+        has_weight(l_run) ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
 }
 
 }  // namespace fi

@@ -110,3 +110,25 @@ def assert_parity(o, lse, o_ref, lse_ref, o_dtype: str, what: str = ""):
         lerr = float(np.max(np.abs(lse[fin] - lse_ref[fin]))) if fin.any() else 0.0
         assert lerr <= LSE_TOL, f"{what}: max |lse - oracle| = {lerr:.3e} > {LSE_TOL}"
     return err
+
+
+def assert_parity_nan(o, lse, o_ref, lse_ref, o_dtype: str, what: str = ""):
+    """Parity where the oracle holds NaNs (a NaN code in the cache): the GPU
+    output is NaN at exactly the oracle's NaN elements of o and lse, and every
+    other element is held to the usual tolerance."""
+    o_nan, l_nan = np.isnan(o_ref), np.isnan(lse_ref)
+    assert o_nan.any(), f"{what}: the case plants no NaN the oracle sees"
+    assert np.array_equal(np.isnan(o), o_nan), \
+        f"{what}: NaN outputs differ from the oracle's ({np.sum(np.isnan(o) != o_nan)} elements)"
+    assert np.array_equal(np.isnan(lse), l_nan), \
+        f"{what}: NaN lse differ from the oracle's ({np.sum(np.isnan(lse) != l_nan)} rows)"
+    return assert_parity(np.where(o_nan, 0.0, o), np.where(l_nan, 0.0, lse), np.where(o_nan, 0.0, o_ref),
+                         np.where(l_nan, 0.0, lse_ref), o_dtype, what)
+
+
+def plant_codes(w: dict, i: int, spots) -> None:
+    """Write stored codes into request i's K or V elements: spots holds
+    (pool name "k_pool" or "v_pool", token, kv head, dimension, code)."""
+    ps = w["page_size"]
+    for pool, t, g, c, code in spots:
+        w[pool][w["indices"][w["indptr"][i] + t // ps], t % ps, g, c] = code

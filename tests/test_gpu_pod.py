@@ -16,8 +16,8 @@ import torch
 
 import oracle.attention as OA
 from attention_paged_fp8_amd import fi
-from workloads import make_paged, make_workload
-from gpu_util import T2, assert_parity, paged_kv, say, upload, workspace_for
+from workloads import NAN_BITS, make_paged, make_workload
+from gpu_util import T2, assert_parity, assert_parity_nan, paged_kv, plant_codes, say, upload, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +171,28 @@ def test_pod_full_size(gpu_device):
     o_ref, l_ref = OA.batch_decode(wd)
     e2 = assert_parity(od, ld, o_ref, l_ref, "f16", "pod full size, decode phase")
     print(f"pod full size: max |o - oracle| prefill {e1:.3e}, decode {e2:.3e}")
+
+
+@pytest.mark.parametrize("ws", [True, False])
+@pytest.mark.parametrize("kvd", ["e4m3", "e4m3fnuz"])
+def test_pod_nan_code_propagates(gpu_device, kvd, ws):
+    """The format's NaN code planted in both phases: in the prefill batch a K
+    element of a key only the later rows see and a V element of a prefix key,
+    in the decode batch a K element of one request (split across pieces or
+    not).  Exactly the oracle's NaN outputs are NaN in both phases, and every
+    other output matches it."""
+    say("pod NaN code", kvd, ws)
+    wp = make_paged(73, qo_lens=[40, 130, 64], prefix_lens=[10, 300, 0], hq=32, hkv=8, d=128, page=16, q="f16",
+                    kvd=kvd, o="f16", extra_pages=2)
+    wd = make_paged(74, kv_lens=[700, 2048, 33, 1500], hq=32, hkv=8, d=128, page=16, q="f16", kvd=kvd, o="f16",
+                    extra_pages=3)
+    plant_codes(wp, 1, [("k_pool", 350, 5, 17, NAN_BITS[kvd]), ("v_pool", 100, 2, 40, NAN_BITS[kvd])])
+    plant_codes(wd, 1, [("k_pool", 1200, 3, 9, NAN_BITS[kvd])])
+    dp, dd = upload(wp, gpu_device), upload(wd, gpu_device)
+    (op, lp), (od, ld) = run_pod(wp, dp, wd, dd, causal=True, workspace=ws)
+    op_ref, lp_ref = OA.batch_prefill(wp, causal=True)
+    od_ref, ld_ref = OA.batch_decode(wd)
+    assert np.isnan(ld_ref).sum() == 4  # the 4 q heads of kv head 3 in decode request 1
+    assert_parity_nan(op, lp, op_ref, lp_ref, "f16", f"pod prefill NaN code {kvd}")
+    assert_parity_nan(od, ld, od_ref, ld_ref, "f16", f"pod decode NaN code {kvd}")
+

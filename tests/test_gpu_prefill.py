@@ -19,9 +19,9 @@ import torch
 
 import oracle.attention as OA
 from oracle.fp8 import fp8_table
-from workloads import make_paged, make_workload
+from workloads import NAN_BITS, make_paged, make_workload
 from attention_paged_fp8_amd import fi
-from gpu_util import T2, assert_parity, paged_kv, run_decode, run_prefill, say, upload
+from gpu_util import T2, assert_parity, assert_parity_nan, paged_kv, plant_codes, run_decode, run_prefill, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,24 @@ def test_causal_prefill_full_size(gpu_device):
     o_ref, l_ref = OA.batch_prefill(w, causal=True)
     err = assert_parity(og, lg, o_ref, l_ref, "f16", "causal-prefill workload")
     print(f"causal-prefill workload: max |o - oracle| = {err:.3e}")
+
+
+@pytest.mark.parametrize("kvd,q", [("e4m3", "f16"), ("e5m2", "bf16"), ("e4m3fnuz", "f16"), ("e5m2fnuz", "bf16")])
+def test_prefill_nan_code_propagates(gpu_device, kvd, q):
+    """The format's NaN code in one K element of a key that only the later
+    query rows see (causal mask), and in one V element of a prefix key that
+    every row sees: the oracle's NaN outputs -- whole rows of that kv head's
+    q heads from the first row that sees the key, and the V element's column
+    of every row -- are NaN, and every other output matches it."""
+    say("prefill NaN code", kvd, q)
+    w = make_paged(37, qo_lens=[40, 130, 64], prefix_lens=[10, 300, 0], hq=32, hkv=8, d=128, page=16, q=q,
+                   kvd=kvd, o=q, extra_pages=2)
+    plant_codes(w, 1, [("k_pool", 350, 5, 17, NAN_BITS[kvd]), ("v_pool", 100, 2, 40, NAN_BITS[kvd])])
+    dv = upload(w, gpu_device)
+    og, lg, _ = run_prefill(w, dv, causal=True)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert np.isnan(l_ref).sum() == (130 - 50) * 4  # rows 50.. of request 1 see key 350
+    assert_parity_nan(og, lg, o_ref, l_ref, q, f"NaN code {kvd}")
 
 
 def test_rows_without_visible_keys(gpu_device):

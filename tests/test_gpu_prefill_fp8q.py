@@ -31,8 +31,8 @@ import pytest
 import torch
 
 import oracle.attention as OA
-from workloads import make_paged, make_workload
-from gpu_util import LSE_TOL, O_TOL, T2, assert_parity, paged_kv, say, upload
+from workloads import NAN_BITS, make_paged, make_workload
+from gpu_util import LSE_TOL, O_TOL, T2, assert_parity, assert_parity_nan, paged_kv, plant_codes, say, upload
 from attention_paged_fp8_amd import fi
 
 pytestmark = pytest.mark.gpu
@@ -252,3 +252,29 @@ def test_ragged_and_single_fp8q_equal_paged(gpu_device, q, kvd, pv8):
                               pv_fp8=pv8, k_scale=w["k_scale"], v_scale=w["v_scale"], kv_dtype=kvd, lse=l1)
     torch.cuda.synchronize()
     assert np.array_equal(o1.double().cpu().numpy(), op[q0:q1]) and np.array_equal(l1.double().cpu().numpy(), lp[q0:q1])
+
+
+@pytest.mark.parametrize("pv_fp8", [False, True])
+@pytest.mark.parametrize("kvd", ["e4m3", "e5m2"])
+def test_fp8q_nan_code_propagates(gpu_device, kvd, pv_fp8):
+    """The cache format's NaN code in one K element of a key only the later
+    rows see and in one V element of a prefix key every row sees, with the
+    raw codes on the fp8 matrix cores: exactly the oracle's NaN outputs are
+    NaN (whole rows from the first row that sees the K code, the V code's
+    column of every row).  With P V in f16 every other output matches the
+    oracle to the usual tolerance; with fp8 P V they are finite (their
+    values are held to the derived bound by the other tests)."""
+    say("fp8q NaN code", kvd, pv_fp8)
+    w = make_paged(38, qo_lens=[40, 130, 64], prefix_lens=[10, 300, 0], hq=32, hkv=8, d=128, page=16, q="e4m3",
+                   kvd=kvd, o="f16", extra_pages=2)
+    plant_codes(w, 1, [("k_pool", 350, 5, 17, NAN_BITS[kvd]), ("v_pool", 100, 2, 40, NAN_BITS[kvd])])
+    dv = upload(w, gpu_device)
+    og, lg = run_fp8q(w, dv, causal=True, pv_fp8=pv_fp8)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert np.isnan(l_ref).sum() == (130 - 50) * 4
+    if not pv_fp8:
+        assert_parity_nan(og, lg, o_ref, l_ref, "f16", f"fp8q NaN code {kvd}")
+        return
+    assert np.array_equal(np.isnan(og), np.isnan(o_ref)) and np.array_equal(np.isnan(lg), np.isnan(l_ref))
+    assert np.isfinite(og[~np.isnan(o_ref)]).all()
+
