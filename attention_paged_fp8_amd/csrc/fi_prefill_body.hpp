@@ -42,7 +42,13 @@ struct PrefillCfg {
   static constexpr int VTILE = TK * VP;
   // two K slots, then two V slots
   static constexpr int K0 = 0, K1 = KTILE, V0 = 2 * KTILE, V1 = 2 * KTILE + VTILE;
-  static constexpr int LDS = 2 * KTILE + 2 * VTILE;
+  // The epilogue stages the normalised output in the same memory: the
+  // workgroup's 256 rows as its query tokens, each token's heads_per_wg rows
+  // contiguous (as in o) and the token pitch padded by 16 bytes (16-byte
+  // aligned pieces; the 32 tokens of a wave's rows spread over 16 bank
+  // groups).  Largest with one head per workgroup (256 tokens).
+  static constexpr int OSTAGE = 256 * (ROW + 16);
+  static constexpr int LDS = (2 * KTILE + 2 * VTILE > OSTAGE) ? 2 * KTILE + 2 * VTILE : OSTAGE;
   static constexpr int NT = 64 * kPrefillWaves;     // threads per workgroup
   static constexpr int CHUNKS = TK * DB / 16;       // 16-byte pieces of a tile of one tensor
   static constexpr int PER = (CHUNKS + NT - 1) / NT;  // per thread (the last round may be partial)
@@ -581,24 +587,45 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
   // ---- epilogue ------------------------------------------------------------
   lr_run = sum_half_swap(lr_run);
   l_run = Cfg::kF32Lse ? sum_half_swap(l_run) : lr_run;
-  if (!row_ok) return;
   const float lnorm = P8 ? l_run : lr_run;  // fp8 probabilities: the fp32 sum
   // a row without visible keys has sums of exactly +0; a NaN read from the
   // cache makes them NaN, which then carries into o and lse
   const float inv = has_weight(lnorm) ? p.v_scale / lnorm : 0.f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(q_begin + qpos) * p.num_qo_heads + hq) * D;
+  // The output goes out through LDS: a lane's own values are 4 dimensions of
+  // one row, and storing them directly scatters each wave store over 32 rows
+  // 32 * num_qo_heads * D bytes apart; staged, a token's heads_per_wg rows
+  // (contiguous in o) leave as whole 16-byte pieces of one run.
+  const int tokp = p.heads_per_wg * Cfg::ROW + 16;  // staging pitch of a token
+  __syncthreads();  // every wave is done with the K/V slots
+  {
+    uint8_t* orow = smem + (qpos - q0) * tokp + head_local * Cfg::ROW;
 #pragma unroll
-  for (int db = 0; db < Cfg::NDB; ++db)
+    for (int db = 0; db < Cfg::NDB; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      // 4 positions, 4 consecutive dimensions (fp8 V^T rows are dimensions)
-      const int d = P8 ? 32 * db + 8 * i4 + 4 * hh : Cfg::dim_of(32 * db + 8 * i4 + 4 * hh);
-      *reinterpret_cast<uint2*>(op + d) = make_uint2(pack2<OBF16>(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv),
-                                                     pack2<OBF16>(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv));
+      for (int i4 = 0; i4 < 4; ++i4) {
+        // 4 positions, 4 consecutive dimensions (fp8 V^T rows are dimensions)
+        const int d = P8 ? 32 * db + 8 * i4 + 4 * hh : Cfg::dim_of(32 * db + 8 * i4 + 4 * hh);
+        *reinterpret_cast<uint2*>(orow + 2 * d) =
+            make_uint2(pack2<OBF16>(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv),
+                       pack2<OBF16>(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv));
+      }
+  }
+  __syncthreads();
+  {
+    const int pieces_shift = __builtin_ctz(p.heads_per_wg * Cfg::ROW / 16);  // 16-byte pieces per token
+    const int ntok = min(p.q_per_wg, qo_len - q0);
+    const int64_t tok_stride = (int64_t)p.num_qo_heads * Cfg::ROW;
+    uint8_t* ob = reinterpret_cast<uint8_t*>(p.o) + ((int64_t)(q_begin + q0) * p.num_qo_heads + hq - head_local) * Cfg::ROW;
+    for (int k = tid; k < (ntok << pieces_shift); k += Cfg::NT) {
+      const int t = k >> pieces_shift;
+      const int c = k - (t << pieces_shift);
+      *reinterpret_cast<uint4*>(ob + t * tok_stride + 16 * c) = *reinterpret_cast<const uint4*>(smem + t * tokp + 16 * c);
     }
-  if (p.lse && hh == 0)
+  }
+  if (p.lse && hh == 0 && row_ok)
     p.lse[(int64_t)(q_begin + qpos) * p.num_qo_heads + hq] =
         has_weight(l_run) ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+  // ---- end of item
 }
 
 }  // namespace fi
