@@ -48,7 +48,14 @@ struct PrefillCfg {
   // aligned pieces; the 32 tokens of a wave's rows spread over 16 bank
   // groups).  Largest with one head per workgroup (256 tokens).
   static constexpr int OSTAGE = 256 * (ROW + 16);
-  static constexpr int LDS = (2 * KTILE + 2 * VTILE > OSTAGE) ? 2 * KTILE + 2 * VTILE : OSTAGE;
+  // The prologue brings the query block in the same way, into its own area
+  // after the slots: each token's heads_per_wg query rows contiguous, token
+  // pitch padded by 16 bytes.
+  static constexpr int QROW = Q8 ? D : 2 * D;       // bytes of a query row
+  static constexpr int QS = 2 * KTILE + 2 * VTILE;  // offset of the query area
+  static constexpr int QSTAGE = 256 * (QROW + 16);
+  static constexpr int QPER = 256 * QROW / 16 / (64 * kPrefillWaves);  // 16-byte query pieces per thread
+  static constexpr int LDS = (QS + QSTAGE > OSTAGE) ? QS + QSTAGE : OSTAGE;
   static constexpr int NT = 64 * kPrefillWaves;     // threads per workgroup
   static constexpr int CHUNKS = TK * DB / 16;       // 16-byte pieces of a tile of one tensor
   static constexpr int PER = (CHUNKS + NT - 1) / NT;  // per thread (the last round may be partial)
@@ -200,20 +207,10 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
   // positions (D/2)*hh + 8s + j, j = 0..7 (8 consecutive dimensions).
   // fp8 query (Q8): for k-step c, lane (hh, rho) holds the 32 bytes of
   // dimensions 64c + 32hh .. +31, in memory order (K rows are read the same way).
+  // Filled in the prologue from the query area of LDS (rows past the block's
+  // queries are zero there).
   uint4 qop[Cfg::NS];
-  if constexpr (Q8) {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
-                        ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D + 32 * hh;
-#pragma unroll
-    for (int s = 0; s < 2 * Cfg::NS8; ++s)
-      qop[s] = row_ok ? *reinterpret_cast<const uint4*>(qp + 64 * (s >> 1) + 16 * (s & 1)) : make_uint4(0, 0, 0, 0);
-  } else {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
-                         ((int64_t)(q_begin + (row_ok ? qpos : 0)) * p.num_qo_heads + hq) * D;
-#pragma unroll
-    for (int s = 0; s < Cfg::NS; ++s)
-      qop[s] = row_ok ? *reinterpret_cast<const uint4*>(qp + Cfg::dim_of((D / 2) * hh + 8 * s)) : make_uint4(0, 0, 0, 0);
-  }
+  const int qtokp = p.heads_per_wg * Cfg::QROW + 16;  // query area pitch of a token
 
   // ---- tile gather ---------------------------------------------------------
   // Chunk ci = j*NT + tid of a tensor's tile is row ci / (DB/16), 16-byte
@@ -543,31 +540,63 @@ __device__ __forceinline__ void prefill_body(const P& p, const int bx, const int
     {
       // tiles 0..3 go out together; 0 and 1 land in LDS, 2 and 3 stay in
       // the register sets of steps 0 and 1
-      uint32_t q0[Cfg::PER], q1[Cfg::PER], q2[Cfg::PER], q3[Cfg::PER];
-      load_pids(0, q0);
-      load_pids(tile_of(1), q1);
-      load_pids(tile_of(2), q2);
-      load_pids(tile_of(3), q3);
+      uint32_t i0[Cfg::PER], i1[Cfg::PER], i2[Cfg::PER], i3[Cfg::PER];
+      load_pids(0, i0);
+      load_pids(tile_of(1), i1);
+      load_pids(tile_of(2), i2);
+      load_pids(tile_of(3), i3);
       load_pids(tile_of(4), pb);
+      // the query block, after the page ids (which the K/V addresses wait
+      // for): whole 16-byte pieces of each token's contiguous head rows
+      const int qshift = __builtin_ctz(p.heads_per_wg * Cfg::QROW / 16);  // pieces per token
+      const int ntok = min(p.q_per_wg, qo_len - q0);
+      const uint8_t* qsrc =
+          reinterpret_cast<const uint8_t*>(p.q) + ((int64_t)(q_begin + q0) * p.num_qo_heads + hq - head_local) * Cfg::QROW;
+      const int64_t qtok_stride = (int64_t)p.num_qo_heads * Cfg::QROW;
+      uint4 qst[Cfg::QPER];
+#pragma unroll
+      for (int k = 0; k < Cfg::QPER; ++k) {
+        const int pc = k * Cfg::NT + tid;
+        const int t = pc >> qshift;
+        qst[k] = t < ntok ? load16(qsrc + t * qtok_stride + 16 * (pc - (t << qshift))) : make_uint4(0, 0, 0, 0);
+      }
       Fetch f0, f1;
-      locate(0, q0);
+      locate(0, i0);
       load_k(f0);
       load_v(f0);
-      locate(tile_of(1), q1);
+      locate(tile_of(1), i1);
       load_k(f1);
       load_v(f1);
-      locate(tile_of(2), q2);
+      locate(tile_of(2), i2);
       load_k(fa);
       load_v(fa);
-      locate(tile_of(3), q3);
+      locate(tile_of(3), i3);
       load_k(fb);
       load_v(fb);
+#pragma unroll
+      for (int k = 0; k < Cfg::QPER; ++k) {
+        const int pc = k * Cfg::NT + tid;
+        const int t = pc >> qshift;
+        *reinterpret_cast<uint4*>(smem + Cfg::QS + t * qtokp + 16 * (pc - (t << qshift))) = qst[k];
+      }
       store_k(f0, K0);
       store_v(f0, V0);
       store_k(f1, K1);
       store_v(f1, V1);
     }
     __syncthreads();
+    {
+      const uint8_t* qrow = smem + Cfg::QS + (qpos - q0) * qtokp + head_local * Cfg::QROW;
+      if constexpr (Q8) {
+#pragma unroll
+        for (int s = 0; s < 2 * Cfg::NS8; ++s)
+          qop[s] = *reinterpret_cast<const uint4*>(qrow + 32 * hh + 64 * (s >> 1) + 16 * (s & 1));
+      } else {
+#pragma unroll
+        for (int s = 0; s < Cfg::NS; ++s)
+          qop[s] = *reinterpret_cast<const uint4*>(qrow + 2 * Cfg::dim_of((D / 2) * hh + 8 * s));
+      }
+    }
     float m_use = 0.f;
     if (ntw > 0) {
       qk(K0, s0);
