@@ -314,12 +314,14 @@ def copy_bandwidth(mb: int = 512, steps: int = 20) -> float:
 
 
 def decode_extra(steps, warmup):
-    """Long-context split-KV decode, the three KV types of the mixed-dtype
-    decode workload, and the batch-decode workload over an e4m3fnuz cache:
-    HIP-event medians and HBM rates (context beside the main line; each is a
-    separate decode workload)."""
+    """The single-decode workload (one request of 64 tokens: launch-bound, so
+    its rate carries no roofline claim), long-context split-KV decode, the
+    three KV types of the mixed-dtype decode workload, and the batch-decode
+    workload over e4m3fnuz and e5m2fnuz caches: HIP-event medians and HBM rates
+    (context beside the main line; each is a separate decode workload)."""
     out = {}
-    for key, wl, kvd, copies in (("long_context", "long_context_decode", None, 2), ("kv_f16", "dtype_decode", "f16", 2),
+    for key, wl, kvd, copies in (("single_decode", "single_decode", None, 1),
+                                 ("long_context", "long_context_decode", None, 2), ("kv_f16", "dtype_decode", "f16", 2),
                                  ("kv_bf16_mixed", "dtype_decode", "bf16", 2), ("kv_e4m3", "dtype_decode", "e4m3", 4),
                                  ("kv_e4m3fnuz", "batch_decode", "e4m3fnuz", 4),
                                  ("kv_e5m2fnuz", "batch_decode", "e5m2fnuz", 4)):
@@ -328,7 +330,7 @@ def decode_extra(steps, warmup):
         med = float(np.median(ev))
         out[key] = {"workload": w["name"] + (f"_kv_{kvd}" if kvd else ""), "bytes_per_call": nb,
                     "us_median": round(med * 1e3, 2), "gbs": round(nb / (med * 1e-3) / 1e9, 1),
-                    "frac": round(nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    "frac": None if key == "single_decode" else round(nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"# {key}: {nb / 1e6:.1f} MB, median {med * 1e3:.1f} us -> {out[key]['gbs']} GB/s", file=sys.stderr,
               flush=True)
         import torch
