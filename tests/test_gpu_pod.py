@@ -8,7 +8,9 @@ workspace, empty requests in both phases); the prefill phase bit-identical
 to fi_batch_prefill_paged on the same inputs; one phase empty; the two
 phases over the same pools with different page tables; and at full size the
 causal-prefill workload with the batch-decode shapes in f16 (16 prefill and
-64 decode requests) in one call, every element against the oracle.
+64 decode requests) in one call, every element against the oracle; NaN codes
+in both phases; phases larger than the geometry (48 requests) and prefix sums
+(256 requests) one launch's arguments carry.
 """
 import numpy as np
 import pytest
@@ -195,4 +197,26 @@ def test_pod_nan_code_propagates(gpu_device, kvd, ws):
     assert np.isnan(ld_ref).sum() == 4  # the 4 q heads of kv head 3 in decode request 1
     assert_parity_nan(op, lp, op_ref, lp_ref, "f16", f"pod prefill NaN code {kvd}")
     assert_parity_nan(od, ld, od_ref, ld_ref, "f16", f"pod decode NaN code {kvd}")
+
+
+def test_pod_past_argument_capacities(gpu_device):
+    """A prefill phase of 60 requests (more than the 48 whose geometry one
+    launch's arguments carry: the prefill workgroups then read it from the
+    device) with a decode phase of 300 requests (more than the 256 token
+    prefix sums carried: every decode workgroup scans the page table itself),
+    against the oracle."""
+    say("pod past argument capacities")
+    rng = np.random.default_rng(79)
+    qo = rng.integers(1, 41, size=60)
+    prefix = rng.integers(0, 101, size=60)
+    dec = rng.integers(0, 201, size=300)
+    wp = make_paged(79, qo_lens=list(qo), prefix_lens=list(prefix), hq=8, hkv=2, d=128, page=16, q="f16", kvd="e4m3",
+                    extra_pages=2)
+    wd = make_paged(80, kv_lens=list(dec), hq=8, hkv=2, d=128, page=16, q="f16", kvd="e4m3", extra_pages=2)
+    dp, dd = upload(wp, gpu_device), upload(wd, gpu_device)
+    (op, lp), (od, ld) = run_pod(wp, dp, wd, dd, causal=True)
+    o_ref, l_ref = OA.batch_prefill(wp, causal=True)
+    assert_parity(op, lp, o_ref, l_ref, "f16", "pod prefill phase, 60 requests")
+    o_ref, l_ref = OA.batch_decode(wd)
+    assert_parity(od, ld, o_ref, l_ref, "f16", "pod decode phase, 300 requests")
 

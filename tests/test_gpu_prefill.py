@@ -10,8 +10,9 @@ without queries or without keys; decode equal to prefill with one query per
 request; run-to-run determinism and page-permutation invariance (bitwise);
 fp8 (OCP and fnuz) equal to the same values stored in the 2-byte type
 (bitwise); fnuz caches in the shape matrix; constant V;
-a head-major pool through its strides; 800 requests, more (request, query
-block) pairs than the dispatch order in the kernel arguments holds.
+a head-major pool through its strides; 200 requests, more than the geometry
+the kernel arguments hold; 800 requests, more (request, query block) pairs
+than the dispatch order in the kernel arguments holds; NaN codes in K and V.
 """
 import numpy as np
 import pytest
@@ -245,6 +246,23 @@ def test_prefill_requests_without_queries_or_keys(gpu_device, causal):
     assert np.all(o[0:40] == 0) and np.all(np.isneginf(l[0:40]))
     o_ref, l_ref = OA.batch_prefill(w, causal=causal)
     assert_parity(o, l, o_ref, l_ref, "bf16", "prefill empty requests")
+
+
+def test_prefill_geometry_from_device(gpu_device):
+    """200 short requests: their (request, query block) pairs fit the dispatch
+    order in the kernel arguments (512) but their geometry does not (96), so
+    the workgroups read each request's rows and pages from the device arrays;
+    against the oracle."""
+    say("prefill 200 requests")
+    rng = np.random.default_rng(200)
+    qo = rng.integers(1, 65, size=200)
+    prefix = rng.integers(0, 200, size=200)
+    w = make_paged(200, qo_lens=list(qo), prefix_lens=list(prefix), hq=8, hkv=2, d=128, page=16, q="f16", kvd="e4m3",
+                   o="f16", extra_pages=2)
+    dv = upload(w, gpu_device)
+    og, lg, _ = run_prefill(w, dv, causal=True)
+    o_ref, l_ref = OA.batch_prefill(w, causal=True)
+    assert_parity(og, lg, o_ref, l_ref, "f16", "200 short requests")
 
 
 def test_prefill_many_query_blocks(gpu_device):
