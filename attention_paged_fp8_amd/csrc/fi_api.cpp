@@ -892,16 +892,21 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
     d.num_qo_heads = num_qo_heads;
     d.num_kv_heads = kv_d->num_kv_heads;
     d.group = num_qo_heads / kv_d->num_kv_heads;
-    // Decode slices first, on few workgroups: the decode stream needs HBM
+    // Decode slices first, on a share of the CUs: the decode stream needs HBM
     // bandwidth rather than CUs, so a fraction of the CUs streams it while the
     // rest start the prefill items, which then fill the CUs the decode
-    // workgroups leave.  The fraction balances the two phases' estimated
-    // durations: decode bytes at kPodDecodeWgRate per 8-wave workgroup against
-    // prefill flops at kPodPrefillCuRate per CU (both measured on MI355X under
-    // sustained load: the causal-prefill workload at ~826 TFLOP/s over 256 CUs;
-    // a lone decode workgroup streams ~20 GB/s).  A decode-only call takes two
-    // workgroups per CU.  FI_POD_DECODE_WG overrides the count.
-    constexpr double kPodPrefillCuRate = 3.2e12, kPodDecodeWgRate = 20e9;
+    // workgroups leave.  The decode phase costs about the same CU time however
+    // many workgroups share it (each streams at its own rate), so the launch
+    // takes about (decode + prefill CU time) / CUs as long as the decode
+    // workgroups finish within it; they are sized to take half that estimate,
+    // which keeps them off the critical path (measured on the mixed batch:
+    // fewer workgroups, sized to end with the prefill, made the decode phase
+    // the longer one on some runs).  Decode bytes at kPodDecodeWgRate per 8-wave
+    // workgroup, prefill flops at kPodPrefillCuRate per CU (both measured on
+    // MI355X under sustained load: the causal-prefill workload at ~890 TFLOP/s
+    // over 256 CUs; a lone decode workgroup streams ~20 GB/s).  A decode-only
+    // call takes two workgroups per CU.  FI_POD_DECODE_WG overrides the count.
+    constexpr double kPodPrefillCuRate = 3.5e12, kPodDecodeWgRate = 20e9;
     const int cus = std::max(1, fi::device_cus());
     int slots = 2 * cus;
     if (pp.n_prefill_wg > 0) {
@@ -915,7 +920,8 @@ fi_status fi_batch_pod_paged(const void* q_p, const int32_t* qo_indptr, const in
       }
       flops *= 4.0 * hd * num_qo_heads;
       const double bytes = (double)total_kv_d * kv_d->num_kv_heads * hd * eb * 2;
-      const double nd = cus * bytes * kPodPrefillCuRate / (flops * kPodDecodeWgRate + bytes * kPodPrefillCuRate);
+      const double dec_cu = bytes / kPodDecodeWgRate, pf_cu = flops / kPodPrefillCuRate;  // CU-seconds
+      const double nd = 2.0 * cus * dec_cu / (dec_cu + pf_cu);
       slots = (int)std::lround(std::min<double>(2.0 * cus, std::max<double>(std::max(8, cus / 16), nd)));
     }
     if (const char* env = std::getenv("FI_POD_DECODE_WG")) {

@@ -586,7 +586,7 @@ def main():
               f"{pod['two_calls_one_stream']} us, on two streams {pod['two_calls_two_streams']} us", file=sys.stderr,
               flush=True)
     if args.only == "all" and not args.no_extra:
-        extra = decode_extra(max(5, args.steps // 2), 3)
+        extra = decode_extra(args.steps, 3)
         copy_gbs = round(copy_bandwidth(), 1)
         print(f"# plain device copy: {copy_gbs} GB/s", file=sys.stderr, flush=True)
 
