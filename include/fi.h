@@ -243,8 +243,9 @@ fi_status fi_batch_prefill_paged(const void* q, fi_dtype q_dtype, const int32_t*
  * for the decode phase (its sentences name "(decode phase)"), then the
  * cross-phase dtype and head checks, shapes and pointers, then workspace.
  * The launch puts the decode slices first, on a share of the compute units
- * sized so that both phases end together (a decode stream needs bandwidth
- * more than CUs), and the prefill items on the rest.
+ * sized so that the decode phase takes about half of the launch's estimated
+ * time (a decode stream needs bandwidth more than CUs), and the prefill items
+ * on the rest and on the units the decode slices leave.
  * Environment: FI_POD_DECODE_WG = a positive count of decode workgroups to
  * cut the decode phase into (default: that share; two per compute unit when
  * the prefill phase is empty); FI_POD_ORDER = "prefill_first" dispatches the
